@@ -1,0 +1,122 @@
+"""Seeded synthetic inputs, shared by the tests, the benchmark and the smoke
+check.  This module holds no arithmetic of the method itself: it only draws
+random tensors with the structure the MiniKV pages describe (an attention
+sink, a few heavy-hitter keys aligned with the queries, and a handful of key
+channels with large outliers -- Pith review of MiniKV, Fig. 10 caption on the
+attention distribution, and the verdict record's supporting citation on
+channel outliers in keys).
+
+Every draw uses numpy's PCG64 seeded with a tuple
+(SEED, config, layer, tag, index) so that any batch element or decode step can
+be regenerated on its own.  Tags: 0 Q, 1 K, 2 V, 3 outlier channels,
+4 heavy-hitter positions, 5/6/7 decode q/k/v, 8 score vectors, 9 selections.
+All tensors are produced in fp32 and rounded once to fp16 (numpy astype, RNE).
+"""
+import numpy as np
+
+from . import configs
+
+SINK_GAIN = 8.0       # sink key = SINK_GAIN * sqrt(D) * u
+HH_GAIN = 4.0         # planted heavy hitters = HH_GAIN * sqrt(D) * u
+N_HH_PLANTED = 8
+N_OUTLIER_CH = 4
+OUTLIER_GAIN = 10.0
+
+
+def rng(*key):
+    return np.random.default_rng([configs.SEED] + [int(x) for x in key])
+
+
+def outlier_channels(cfg_id, layer, Hkv, D):
+    """[Hkv][N_OUTLIER_CH] distinct key channels per kv head."""
+    r = rng(cfg_id, layer, 3)
+    nch = min(N_OUTLIER_CH, D)
+    return np.stack([np.sort(r.choice(D, nch, replace=False))
+                     for _ in range(Hkv)])
+
+
+def gen_unit_batch(cfg_id, layer, b, Hq, Hkv, n, D, r_window,
+                   structure=True):
+    """Q [Hq][n][D], K, V [Hkv][n][D] (fp16) for batch element b."""
+    g = Hq // Hkv
+    q = rng(cfg_id, layer, 0, b).standard_normal((Hq, n, D), np.float32)
+    k = rng(cfg_id, layer, 1, b).standard_normal((Hkv, n, D), np.float32)
+    v = rng(cfg_id, layer, 2, b).standard_normal((Hkv, n, D), np.float32)
+    if structure and n > 0:
+        hr = rng(cfg_id, layer, 4, b)
+        och = outlier_channels(cfg_id, layer, Hkv, D)
+        for h in range(Hkv):
+            u = q[h * g:(h + 1) * g].mean(axis=(0, 1), dtype=np.float64)
+            nu = np.linalg.norm(u)
+            u = (u / nu if nu > 0 else np.ones(D) / np.sqrt(D)).astype(np.float32)
+            k[h, 0] = SINK_GAIN * np.sqrt(D) * u
+            hi = max(n - r_window, 1)
+            cnt = min(N_HH_PLANTED, hi - 1)
+            if cnt > 0:
+                pos = hr.choice(np.arange(1, hi), cnt, replace=False)
+                k[h, pos] = HH_GAIN * np.sqrt(D) * u
+            k[h][:, och[h]] *= OUTLIER_GAIN
+    return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
+
+
+def gen_prefill(cfg_id, layer, batches=None, structure=True, c=None):
+    """Q [nb][Hq][n][D], K, V [nb][Hkv][n][D] fp16 for the listed batches."""
+    c = c or configs.get(cfg_id)
+    batches = range(c["B"]) if batches is None else batches
+    r_window = c["n"] * c["rw"][0] // c["rw"][1]
+    parts = [gen_unit_batch(cfg_id, layer, b, c["Hq"], c["Hkv"], c["n"],
+                            c["D"], r_window, structure) for b in batches]
+    return tuple(np.stack(x) for x in zip(*parts))
+
+
+def gen_decode_step(cfg_id, layer, step, B, Hq, Hkv, D, structure=True):
+    """q [B][Hq][D], k, v [B][Hkv][D] fp16 for one decode step."""
+    q = rng(cfg_id, layer, 5, step).standard_normal((B, Hq, D), np.float32)
+    k = rng(cfg_id, layer, 6, step).standard_normal((B, Hkv, D), np.float32)
+    v = rng(cfg_id, layer, 7, step).standard_normal((B, Hkv, D), np.float32)
+    if structure:
+        och = outlier_channels(cfg_id, layer, Hkv, D)
+        for h in range(Hkv):
+            k[:, h][:, och[h]] *= OUTLIER_GAIN
+    return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
+
+
+def gen_scores(seed, units, n, kind="random"):
+    """fp32 cumulative-score-like vectors [units][n] for selection tests.
+
+    kind: "random" (distinct-ish positive values), "ties" (values from a set
+    of 7 levels, so ties are everywhere), "const" (all equal),
+    "decreasing" (strictly decreasing in the index).
+    """
+    r = rng(8, seed)
+    if kind == "random":
+        x = r.exponential(1.0, (units, n)).astype(np.float32)
+    elif kind == "ties":
+        x = r.integers(0, 7, (units, n)).astype(np.float32) * 0.25
+    elif kind == "const":
+        x = np.full((units, n), 1.5, np.float32)
+    elif kind == "decreasing":
+        x = np.tile(np.linspace(1000.0, 1.0, n, dtype=np.float32), (units, 1))
+    else:
+        raise ValueError(kind)
+    return np.ascontiguousarray(x)
+
+
+def gen_selection(seed, units, n, m):
+    """Random ascending index sets [units][m] drawn from [0, n)."""
+    r = rng(9, seed)
+    return np.stack([np.sort(r.choice(n, m, replace=False)).astype(np.int32)
+                     for _ in range(units)])
+
+
+def gen_kv(seed, units, n, D, outliers=True):
+    """Plain fp16 K, V [units][n][D] for codec tests (N(0,1), a few key
+    channels scaled by OUTLIER_GAIN)."""
+    r = rng(10, seed)
+    k = r.standard_normal((units, n, D), np.float32)
+    v = r.standard_normal((units, n, D), np.float32)
+    if outliers:
+        for u in range(units):
+            ch = r.choice(D, min(N_OUTLIER_CH, D), replace=False)
+            k[u][:, ch] *= OUTLIER_GAIN
+    return k.astype(np.float16), v.astype(np.float16)

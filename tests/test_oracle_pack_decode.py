@@ -1,0 +1,177 @@
+"""Pins of the oracle's pack, append/flush and decode.
+
+- Word layout: groups built so their codes are known in advance (exact
+  arithmetic progressions) must produce the words an independent shift-and-or
+  in this test builds from those codes -- keys along tokens, values along
+  channels, element e at bits 2e..2e+1.
+- Ragged tail: the last m mod Gk selected tokens land, unchanged, in the fp16
+  residual.
+- Flush: appending residual_cap tokens packs exactly what pack() of those
+  tokens produces.
+- Decode: with nothing packed it is exact attention over the residual (torch
+  SDPA, fp64); with q = 0 it is the mean of the dequantised values; equal q
+  across a GQA group gives equal outputs; in general it matches torch SDPA
+  over K/V dequantised by an independent numpy unpacker.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_attention_two_amd import synth
+
+
+def _unpack_keys(kq, ks, kz, n_packed, Gk):
+    """Independent numpy unpacker for key words -> fp32 values [n][D]."""
+    D = kq.shape[-1]
+    t = np.arange(n_packed)
+    codes = (kq[t // 16, :] >> (2 * (t % 16))[:, None].astype(np.uint32)) & 3
+    s = ks[t // Gk].view(np.float16).astype(np.float32)
+    z = kz[t // Gk].view(np.float16).astype(np.float32)
+    return codes.astype(np.float32) * s + z
+
+
+def _unpack_values(vq, vs, vz, n_packed, Gv):
+    D = vq.shape[-1] * 16
+    c = np.arange(D)
+    codes = (vq[:n_packed][:, c // 16] >> (2 * (c % 16)).astype(np.uint32)) & 3
+    s = vs[:n_packed][:, c // Gv].view(np.float16).astype(np.float32)
+    z = vz[:n_packed][:, c // Gv].view(np.float16).astype(np.float32)
+    return codes.astype(np.float32) * s + z
+
+
+def test_pack_word_layout_known_codes(oracle):
+    n, D, Gk, Gv = 64, 32, 16, 16
+    r = np.random.default_rng(0)
+    codes_k = r.integers(0, 4, (n, D))
+    codes_v = r.integers(0, 4, (n, D))
+    # force every group to contain both 0 and 3 so scale = 1/4 exactly
+    codes_k[0::16, :] = 0
+    codes_k[1::16, :] = 3
+    codes_v[:, 0::16] = 0
+    codes_v[:, 1::16] = 3
+    k = (codes_k * 0.25 - 1.0).astype(np.float16)
+    v = (codes_v * 0.25 + 2.0).astype(np.float16)
+    sel = np.arange(n, dtype=np.int32)
+    out = oracle.pack_unit(k, v, sel, Gk, Gv)
+    kq = np.zeros((n // 16, D), np.uint32)
+    for t in range(n):
+        kq[t // 16] |= (codes_k[t].astype(np.uint32) << (2 * (t % 16)))
+    vq = np.zeros((n, D // 16), np.uint32)
+    for c in range(D):
+        vq[:, c // 16] |= (codes_v[:, c].astype(np.uint32) << (2 * (c % 16)))
+    assert np.array_equal(out["kq"], kq)
+    assert np.array_equal(out["vq"], vq)
+    assert np.all(out["ks"].view(np.float16) == 0.25)
+    assert np.all(out["kz"].view(np.float16) == -1.0)
+    assert np.all(out["vs"].view(np.float16) == 0.25)
+    assert np.all(out["vz"].view(np.float16) == 2.0)
+
+
+@pytest.mark.parametrize("Gk", [16, 32])
+def test_pack_gather_and_ragged_tail(oracle, Gk):
+    n, D, Gv = 200, 64, 16
+    k, v = synth.gen_kv(4, 1, n, D)
+    sel = synth.gen_selection(5, 1, n, 75)[0]
+    out = oracle.pack_unit(k[0], v[0], sel, Gk, Gv)
+    mp = (75 // Gk) * Gk
+    assert out["vq"].shape[0] == mp
+    assert np.array_equal(out["kres"], k[0][sel[mp:]].view(np.uint16))
+    assert np.array_equal(out["vres"], v[0][sel[mp:]].view(np.uint16))
+    # gather: packing sel equals packing the gathered rows with identity
+    ident = np.arange(75, dtype=np.int32)
+    out2 = oracle.pack_unit(k[0][sel], v[0][sel], ident, Gk, Gv)
+    for key in out:
+        assert np.array_equal(out[key], out2[key])
+    # dequantised values stay within the codec's half-scale bound
+    kh = _unpack_keys(out["kq"], out["ks"], out["kz"], mp, Gk)
+    sc = out["ks"].view(np.float16).astype(np.float64)[np.arange(mp) // Gk]
+    err = np.abs(kh - k[0][sel[:mp]].astype(np.float64))
+    assert np.all(err <= sc / 2 * (1 + 1e-3) + 1e-6)
+
+
+def test_append_flush_equals_pack(oracle):
+    B, Hkv, D, Gk, Gv, nr = 1, 2, 32, 16, 16, 32
+    cache = oracle.OracleCache(B, Hkv, D, Gk, Gv, capacity=96,
+                               residual_cap=nr)
+    k, v = synth.gen_kv(6, B * Hkv, 3 * nr, D)
+    k = k.reshape(B, Hkv, 3 * nr, D)
+    v = v.reshape(B, Hkv, 3 * nr, D)
+    sel = np.tile(np.arange(40, dtype=np.int32), (B, Hkv, 1))
+    cache.pack(k, v, sel)                       # 32 packed + 8 residual
+    assert (cache.n_packed, cache.n_res) == (32, 8)
+    for t in range(40, 64):
+        cache.append(k[:, :, t], v[:, :, t])
+    assert (cache.n_packed, cache.n_res) == (64, 0)
+    ref = oracle.pack_unit(k[0, 1, 32:64], v[0, 1, 32:64],
+                           np.arange(32, dtype=np.int32), Gk, Gv)
+    assert np.array_equal(cache.kq[0, 1, 2:4], ref["kq"])
+    assert np.array_equal(cache.ks[0, 1, 2:4], ref["ks"])
+    assert np.array_equal(cache.vq[0, 1, 32:64], ref["vq"])
+    assert np.array_equal(cache.vz[0, 1, 32:64], ref["vz"])
+    for t in range(64, 96):
+        cache.append(k[:, :, t], v[:, :, t])
+    assert cache.n_packed == 96
+    with pytest.raises(ValueError):
+        for t in range(32):
+            cache.append(k[:, :, t], v[:, :, t])
+
+
+def _sdpa(q, K, V):
+    q = torch.from_numpy(np.asarray(q, np.float64))[:, None, :]
+    K = torch.from_numpy(np.asarray(K, np.float64))
+    V = torch.from_numpy(np.asarray(V, np.float64))
+    g = q.shape[0]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q, K.expand(g, *K.shape), V.expand(g, *V.shape))
+    return o[:, 0].numpy()
+
+
+def test_decode_residual_only_is_exact_attention(oracle):
+    D, g = 64, 3
+    r = np.random.default_rng(1)
+    q = r.standard_normal((g, D)).astype(np.float16)
+    kres = (r.standard_normal((20, D)) * 2).astype(np.float16)
+    vres = r.standard_normal((20, D)).astype(np.float16)
+    z32 = np.zeros((0, D), np.uint32)
+    z16 = np.zeros((0, D), np.uint16)
+    o = oracle.decode_unit(q, 16, 16, 0, z32, z16, z16,
+                           np.zeros((0, D // 16), np.uint32),
+                           np.zeros((0, D // 16), np.uint16),
+                           np.zeros((0, D // 16), np.uint16), 20, kres, vres)
+    np.testing.assert_allclose(o, _sdpa(q.astype(np.float64), kres, vres),
+                               rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("Gk,g", [(16, 1), (32, 4)])
+def test_decode_vs_sdpa_over_independent_dequant(oracle, Gk, g):
+    n, D, Gv, m = 300, 64, 16, 150
+    k, v = synth.gen_kv(8, 1, n, D)
+    sel = synth.gen_selection(9, 1, n, m)[0]
+    out = oracle.pack_unit(k[0], v[0], sel, Gk, Gv)
+    mp = (m // Gk) * Gk
+    r = np.random.default_rng(2)
+    q = r.standard_normal((g, D)).astype(np.float16)
+    o = oracle.decode_unit(q, Gk, Gv, mp, out["kq"], out["ks"], out["kz"],
+                           out["vq"], out["vs"], out["vz"], m - mp,
+                           out["kres"], out["vres"])
+    K = np.concatenate([_unpack_keys(out["kq"], out["ks"], out["kz"], mp, Gk),
+                        out["kres"].view(np.float16).astype(np.float32)])
+    V = np.concatenate([_unpack_values(out["vq"], out["vs"], out["vz"], mp,
+                                       Gv),
+                        out["vres"].view(np.float16).astype(np.float32)])
+    np.testing.assert_allclose(o, _sdpa(q.astype(np.float64), K, V),
+                               rtol=1e-11, atol=1e-12)
+    # q = 0: uniform weights, mean of the dequantised rows
+    o0 = oracle.decode_unit(np.zeros((g, D), np.float16), Gk, Gv, mp,
+                            out["kq"], out["ks"], out["kz"], out["vq"],
+                            out["vs"], out["vz"], m - mp, out["kres"],
+                            out["vres"])
+    np.testing.assert_allclose(o0, np.broadcast_to(V.astype(np.float64)
+                                                   .mean(0), (g, D)),
+                               rtol=1e-12, atol=1e-13)
+    # identical queries across the group -> identical outputs
+    qs = np.broadcast_to(q[:1], (g, D)).copy()
+    os_ = oracle.decode_unit(qs, Gk, Gv, mp, out["kq"], out["ks"], out["kz"],
+                             out["vq"], out["vs"], out["vz"], m - mp,
+                             out["kres"], out["vres"])
+    assert np.all(os_ == os_[:1])
