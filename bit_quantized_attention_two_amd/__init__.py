@@ -12,6 +12,6 @@ __version__ = "0.1.0"
 
 def __getattr__(name):
     if name == "minikv":
-        from . import minikv
-        return minikv
+        import importlib
+        return importlib.import_module(__name__ + ".minikv")
     raise AttributeError(name)

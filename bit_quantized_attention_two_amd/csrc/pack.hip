@@ -1,0 +1,224 @@
+// INT2 asymmetric packing of selected KV tokens (KIVI-style), gfx950.
+//
+// Pith review of MiniKV, "Assumptions & free parameters": keys are quantised
+// per channel over groups of 16 tokens, values per token over groups of 16
+// channels; verdict record, key_machinery: sixteen 2-bit codes per 32-bit
+// word with fp16 scale and zero-point; supporting citation of KIVI: 2-bit
+// asymmetric quantisation.
+//
+// The codec must agree bit for bit with a separately written reference, so
+// every fp32 operation below is a single round-to-nearest-even operation in
+// a fixed order: range = max - min, s = range / 3 (correctly rounded
+// division), scale = fp16(s), zero = min + 0 (turns -0 into +0), and the code
+// of x is decided by exact comparisons of d = x - zero against (c + 1/2) *
+// scale (exact products), i.e. round-half-even of d / scale clamped to
+// [0, 3].  Contraction into FMAs is switched off for this file.
+#pragma clang fp contract(off)
+
+#include "common.h"
+#include "launch.h"
+
+namespace minikv {
+namespace {
+
+struct QParams {
+    uint16_t sh, zh;
+    float sf, zf, t0, t1, t2;
+};
+
+__device__ __forceinline__ QParams qparams(float mn, float mx) {
+    QParams p;
+    float range = __fsub_rn(mx, mn);
+    float s32 = __fdiv_rn(range, 3.0f);
+    p.sh = f2h_bits(s32);
+    p.zh = f2h_bits(__fadd_rn(mn, 0.0f));
+    p.sf = h2f(p.sh);
+    p.zf = h2f(p.zh);
+    p.t0 = __fmul_rn(0.5f, p.sf);
+    p.t1 = __fmul_rn(1.5f, p.sf);
+    p.t2 = __fmul_rn(2.5f, p.sf);
+    return p;
+}
+
+__device__ __forceinline__ uint32_t code_of(float x, const QParams &p) {
+    if (p.sf == 0.0f) return 0u;
+    float d = __fsub_rn(x, p.zf);
+    return (uint32_t)(d > p.t0) + (uint32_t)(d >= p.t1) +
+           (uint32_t)(d > p.t2);
+}
+
+// Keys: one thread per (key group, channel).  The group's Gk source rows are
+// read twice (min/max, then codes); both reads are coalesced across the
+// channel-contiguous threads and the second hits the cache.
+template <int D>
+__global__ __launch_bounds__(256) void pack_keys_kernel(
+    PackSrc src, int n_groups, int dst_group_off, CacheView c) {
+    constexpr int GPB = 256 / D;                 // groups per block
+    const int unit = blockIdx.y;
+    const int gi = blockIdx.x * GPB + threadIdx.x / D;
+    const int ch = threadIdx.x % D;
+    if (gi >= n_groups) return;
+    const int Gk = c.Gk;
+    const uint16_t *base = src.k + (size_t)unit * src.src_unit + ch;
+    const int32_t *sel = src.sel ? src.sel + (size_t)unit * src.sel_unit
+                                 : nullptr;
+    const int p0 = gi * Gk;
+
+    float mn = 0.f, mx = 0.f;
+    for (int t = 0; t < Gk; ++t) {
+        const int row = sel ? sel[p0 + t] : p0 + t;
+        const float x = h2f(base[(size_t)row * D]);
+        if (t == 0) {
+            mn = x;
+            mx = x;
+        } else {
+            if (x < mn) mn = x;
+            if (x > mx) mx = x;
+        }
+    }
+    const QParams qp = qparams(mn, mx);
+
+    const int g_out = dst_group_off + gi;
+    int32_t *kq = c.kq + (size_t)unit * c.kq_unit() +
+                  (size_t)(g_out * Gk / 16) * D + ch;
+    for (int w = 0; w < Gk / 16; ++w) {
+        uint32_t word = 0;
+        for (int e = 0; e < 16; ++e) {
+            const int p = p0 + w * 16 + e;
+            const int row = sel ? sel[p] : p;
+            word |= code_of(h2f(base[(size_t)row * D]), qp) << (2 * e);
+        }
+        kq[(size_t)w * D] = (int32_t)word;
+    }
+    const size_t mo = (size_t)unit * c.km_unit() + (size_t)g_out * D + ch;
+    c.ks[mo] = qp.sh;
+    c.kz[mo] = qp.zh;
+}
+
+// Values: one thread per (token, channel group); the group's Gv halves are
+// read with 16-byte loads.
+template <int D>
+__global__ __launch_bounds__(256) void pack_values_kernel(
+    PackSrc src, int n_tok, int dst_off, CacheView c) {
+    const int unit = blockIdx.y;
+    const int Gv = c.Gv;
+    const int gpt = D / Gv;                      // groups per token
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int p = idx / gpt;
+    const int G = idx % gpt;
+    if (p >= n_tok) return;
+    const int row = src.sel ? src.sel[(size_t)unit * src.sel_unit + p] : p;
+    const uint4 *x4 = reinterpret_cast<const uint4 *>(
+        src.v + (size_t)unit * src.src_unit + (size_t)row * D + G * Gv);
+
+    float mn = 0.f, mx = 0.f;
+    for (int i = 0; i < Gv / 8; ++i) {
+        const uint4 q = x4[i];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        for (int j = 0; j < 8; ++j) {
+            const float x = h2f((uint16_t)(w[j / 2] >> (16 * (j & 1))));
+            if (i == 0 && j == 0) {
+                mn = x;
+                mx = x;
+            } else {
+                if (x < mn) mn = x;
+                if (x > mx) mx = x;
+            }
+        }
+    }
+    const QParams qp = qparams(mn, mx);
+
+    const int t_out = dst_off + p;
+    int32_t *vq = c.vq + (size_t)unit * c.vq_unit() +
+                  (size_t)t_out * (D / 16) + G * Gv / 16;
+    for (int wi = 0; wi < Gv / 16; ++wi) {
+        uint32_t word = 0;
+        for (int h = 0; h < 2; ++h) {
+            const uint4 q = x4[wi * 2 + h];
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+            for (int j = 0; j < 8; ++j) {
+                const float x = h2f((uint16_t)(w[j / 2] >> (16 * (j & 1))));
+                word |= code_of(x, qp) << (2 * (h * 8 + j));
+            }
+        }
+        vq[wi] = (int32_t)word;
+    }
+    const size_t mo = (size_t)unit * c.vm_unit() + (size_t)t_out * gpt + G;
+    c.vs[mo] = qp.sh;
+    c.vz[mo] = qp.zh;
+}
+
+// Copy n_tail source rows (after the packed ones) into residual slots.
+__global__ __launch_bounds__(256) void copy_tail_kernel(
+    PackSrc src, int p_first, int n_tail, CacheView c) {
+    const int unit = blockIdx.y;
+    const int per_row = c.D / 8;                 // uint4 per row
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int slot = idx / per_row;
+    const int part = idx % per_row;
+    if (slot >= n_tail) return;
+    const int p = p_first + slot;
+    const int row = src.sel ? src.sel[(size_t)unit * src.sel_unit + p] : p;
+    const size_t s_off = (size_t)unit * src.src_unit + (size_t)row * c.D;
+    const size_t d_off = (size_t)unit * c.res_unit() + (size_t)slot * c.D;
+    reinterpret_cast<uint4 *>(c.kres + d_off)[part] =
+        reinterpret_cast<const uint4 *>(src.k + s_off)[part];
+    reinterpret_cast<uint4 *>(c.vres + d_off)[part] =
+        reinterpret_cast<const uint4 *>(src.v + s_off)[part];
+}
+
+__global__ __launch_bounds__(256) void append_copy_kernel(
+    const uint16_t *k_new, const uint16_t *v_new, int units, int slot,
+    CacheView c) {
+    const int per_row = c.D / 8;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int unit = idx / per_row;
+    const int part = idx % per_row;
+    if (unit >= units) return;
+    const size_t d_off = (size_t)unit * c.res_unit() + (size_t)slot * c.D;
+    reinterpret_cast<uint4 *>(c.kres + d_off)[part] =
+        reinterpret_cast<const uint4 *>(k_new + (size_t)unit * c.D)[part];
+    reinterpret_cast<uint4 *>(c.vres + d_off)[part] =
+        reinterpret_cast<const uint4 *>(v_new + (size_t)unit * c.D)[part];
+}
+
+}  // namespace
+
+hipError_t launch_pack(const PackSrc &src, int units, int n_tok, int n_tail,
+                       int dst_off, const CacheView &c, hipStream_t stream) {
+    if (n_tok > 0) {
+        const int n_groups = n_tok / c.Gk;
+        const int gpb = 256 / c.D;
+        dim3 gk((n_groups + gpb - 1) / gpb, units);
+        const int vthreads = n_tok * (c.D / c.Gv);
+        dim3 gv((vthreads + 255) / 256, units);
+        if (c.D == 128) {
+            pack_keys_kernel<128><<<gk, 256, 0, stream>>>(
+                src, n_groups, dst_off / c.Gk, c);
+            pack_values_kernel<128><<<gv, 256, 0, stream>>>(src, n_tok,
+                                                            dst_off, c);
+        } else {
+            pack_keys_kernel<64><<<gk, 256, 0, stream>>>(
+                src, n_groups, dst_off / c.Gk, c);
+            pack_values_kernel<64><<<gv, 256, 0, stream>>>(src, n_tok,
+                                                           dst_off, c);
+        }
+    }
+    if (n_tail > 0) {
+        const int threads = n_tail * (c.D / 8);
+        dim3 gt((threads + 255) / 256, units);
+        copy_tail_kernel<<<gt, 256, 0, stream>>>(src, n_tok, n_tail, c);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_append_copy(const uint16_t *k_new, const uint16_t *v_new,
+                              int units, int slot, const CacheView &c,
+                              hipStream_t stream) {
+    const int threads = units * (c.D / 8);
+    append_copy_kernel<<<(threads + 255) / 256, 256, 0, stream>>>(
+        k_new, v_new, units, slot, c);
+    return hipGetLastError();
+}
+
+}  // namespace minikv

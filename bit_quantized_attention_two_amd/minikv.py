@@ -1,0 +1,310 @@
+"""ctypes binding of libminikv.so (include/minikv.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  The binding refuses to work without the built library -- there is
+no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libminikv.so")
+
+OK, EINVAL, EUNSUPPORTED, ECAPACITY, EHIP = 0, -1, -2, -3, -4
+
+_i32 = ctypes.c_int32
+_P = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+class MiniKVError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s: %s" % (status_str(status) if _lib else status,
+                                     msg))
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32),
+                ("head_dim", _i32), ("group_k", _i32), ("group_v", _i32),
+                ("residual_cap", _i32)]
+
+    @property
+    def units(self):
+        return self.batch * self.n_kv_heads
+
+    @property
+    def g(self):
+        return self.n_q_heads // self.n_kv_heads
+
+
+class _CacheC(ctypes.Structure):
+    _fields_ = [("kq", _P), ("k_scale", _P), ("k_zero", _P), ("vq", _P),
+                ("v_scale", _P), ("v_zero", _P), ("k_res", _P), ("v_res", _P),
+                ("capacity", _i32), ("n_packed", _i32), ("n_res", _i32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libminikv.so (build it first: python -m
+    bit_quantized_attention_two_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libminikv.so is not built (%s); run "
+                               "`python -m bit_quantized_attention_two_amd."
+                               "build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        D = ctypes.POINTER(Dims)
+        C = ctypes.POINTER(_CacheC)
+        sig = {
+            "minikv_version": ([], _i32),
+            "minikv_status_str": ([_i32], ctypes.c_char_p),
+            "minikv_last_error": ([], ctypes.c_char_p),
+            "minikv_pyramid_budgets": ([_i32] * 8 + [_P, _P], _i32),
+            "minikv_cache_bytes_closed_form": ([_i32] * 9 + [_P, _P], _i32),
+            "minikv_cache_layout": ([D, _i32, _P], _i32),
+            "minikv_prefill_ws_bytes": ([D, _i32, _i32, _P], _i32),
+            "minikv_decode_ws_bytes": ([D, _i32, _P], _i32),
+            "minikv_prefill_attn": ([D, _i32, _P, _P, _P, _P, _P, _P, _P],
+                                    _i32),
+            "minikv_select": ([D, _i32, _P, _i32, _i32, _P, _P], _i32),
+            "minikv_prefill_select": ([D, _i32, _P, _P, _P, _P, _P, _P, _i32,
+                                       _i32, _P, _P, _sz, _P], _i32),
+            "minikv_pack": ([D, _i32, _P, _P, _P, _i32, C, _P], _i32),
+            "minikv_append": ([D, C, _P, _P, _P], _i32),
+            "minikv_decode_attn": ([D, C, _P, _P, _P, _sz, _P], _i32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("minikv_version", "minikv_status_str", "minikv_last_error",
+            "minikv_pyramid_budgets", "minikv_cache_bytes_closed_form",
+            "minikv_cache_layout", "minikv_prefill_ws_bytes",
+            "minikv_decode_ws_bytes", "minikv_prefill_attn", "minikv_select",
+            "minikv_prefill_select", "minikv_pack", "minikv_append",
+            "minikv_decode_attn")
+
+
+def status_str(s):
+    return lib().minikv_status_str(s).decode()
+
+
+def _check(status):
+    if status != OK:
+        raise MiniKVError(status, lib().minikv_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else _P(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _P(stream.cuda_stream)
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or \
+            not t.is_contiguous() or not t.is_cuda:
+        raise ValueError("%s must be a contiguous CUDA %s tensor of shape %s "
+                         "(got %s %s)" % (name, dtype, tuple(shape), t.dtype,
+                                          tuple(t.shape)))
+
+
+def make_dims(B, Hq, Hkv, D, Gk=16, Gv=16, residual_cap=128):
+    return Dims(B, Hq, Hkv, D, Gk, Gv, residual_cap)
+
+
+# ----------------------------------------------------------- host helpers --
+
+def pyramid_budgets(n, n_layers, hh=(1, 4), rw=(1, 4), depth=7,
+                    pyramid=True):
+    k = (ctypes.c_int32 * n_layers)()
+    r = ctypes.c_int32()
+    _check(lib().minikv_pyramid_budgets(n, n_layers, hh[0], hh[1], rw[0],
+                                        rw[1], depth, 1 if pyramid else 0,
+                                        ctypes.cast(k, _P),
+                                        ctypes.cast(ctypes.pointer(r), _P)))
+    return list(k), r.value
+
+
+def cache_bytes_closed_form(n_layers, n_heads, head_dim, lprompt, lgen,
+                            budget=(1, 2), bits=2, group=16):
+    a, b = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib().minikv_cache_bytes_closed_form(
+        n_layers, n_heads, head_dim, lprompt, lgen, budget[0], budget[1],
+        bits, group, ctypes.cast(ctypes.pointer(a), _P),
+        ctypes.cast(ctypes.pointer(b), _P)))
+    return a.value, b.value
+
+
+def cache_layout(dims, capacity):
+    out = (ctypes.c_size_t * 8)()
+    _check(lib().minikv_cache_layout(ctypes.byref(dims), capacity,
+                                     ctypes.cast(out, _P)))
+    return list(out)
+
+
+def prefill_ws_bytes(dims, n, lse_given=False):
+    out = ctypes.c_size_t()
+    _check(lib().minikv_prefill_ws_bytes(ctypes.byref(dims), n,
+                                         1 if lse_given else 0,
+                                         ctypes.cast(ctypes.pointer(out), _P)))
+    return out.value
+
+
+def decode_ws_bytes(dims, capacity):
+    out = ctypes.c_size_t()
+    _check(lib().minikv_decode_ws_bytes(ctypes.byref(dims), capacity,
+                                        ctypes.cast(ctypes.pointer(out), _P)))
+    return out.value
+
+
+# ----------------------------------------------------------------- caches --
+
+class LayerCache:
+    """Device arrays of one layer's compressed cache plus the host counters
+    (layout in include/minikv.h)."""
+
+    NAMES = ("kq", "k_scale", "k_zero", "vq", "v_scale", "v_zero", "k_res",
+             "v_res")
+
+    def __init__(self, dims, capacity, device="cuda"):
+        self.dims = dims
+        sizes = cache_layout(dims, capacity)
+        U, D = dims.units, dims.head_dim
+        Gk, Gv, nr = dims.group_k, dims.group_v, dims.residual_cap
+        shapes = {
+            "kq": ((U, capacity // 16, D), torch.int32),
+            "k_scale": ((U, capacity // Gk, D), torch.float16),
+            "k_zero": ((U, capacity // Gk, D), torch.float16),
+            "vq": ((U, capacity, D // 16), torch.int32),
+            "v_scale": ((U, capacity, D // Gv), torch.float16),
+            "v_zero": ((U, capacity, D // Gv), torch.float16),
+            "k_res": ((U, nr, D), torch.float16),
+            "v_res": ((U, nr, D), torch.float16),
+        }
+        for name, nbytes in zip(self.NAMES, sizes):
+            shape, dt = shapes[name]
+            t = torch.zeros(shape, dtype=dt, device=device)
+            assert t.numel() * t.element_size() == nbytes
+            setattr(self, name, t)
+        self.c = _CacheC(*[_P(getattr(self, n).data_ptr()) for n in self.NAMES],
+                         capacity, 0, 0)
+
+    @property
+    def capacity(self):
+        return self.c.capacity
+
+    @property
+    def n_packed(self):
+        return self.c.n_packed
+
+    @property
+    def n_res(self):
+        return self.c.n_res
+
+    def nbytes(self):
+        return sum(getattr(self, n).numel() * getattr(self, n).element_size()
+                   for n in self.NAMES)
+
+
+# ---------------------------------------------------------- compute calls --
+
+def prefill_attn(dims, q, k, v, o=None, lse=None, col=None, stream=None):
+    B, Hq, Hkv, D = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    n = q.shape[2]
+    _need(q, torch.float16, (B, Hq, n, D), "q")
+    _need(k, torch.float16, (B, Hkv, n, D), "k")
+    _need(v, torch.float16, (B, Hkv, n, D), "v")
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device) \
+        if lse is None else lse
+    col = torch.empty((B, Hkv, n), dtype=torch.float32, device=q.device) \
+        if col is None else col
+    _check(lib().minikv_prefill_attn(ctypes.byref(dims), n, _ptr(q), _ptr(k),
+                                     _ptr(v), _ptr(o), _ptr(lse), _ptr(col),
+                                     _stream(stream)))
+    return o, lse, col
+
+
+def select(dims, col, n_hh, n_recent, sel=None, stream=None):
+    B, Hkv = dims.batch, dims.n_kv_heads
+    n = col.shape[-1]
+    _need(col, torch.float32, (B, Hkv, n), "col")
+    sel = torch.empty((B, Hkv, n_hh + n_recent), dtype=torch.int32,
+                      device=col.device) if sel is None else sel
+    _check(lib().minikv_select(ctypes.byref(dims), n, _ptr(col), n_hh,
+                               n_recent, _ptr(sel), _stream(stream)))
+    return sel
+
+
+def prefill_select(dims, q, k, v, n_hh, n_recent, o=None, col=None, lse=None,
+                   sel=None, ws=None, stream=None):
+    B, Hq, Hkv, D = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    n = q.shape[2]
+    _need(q, torch.float16, (B, Hq, n, D), "q")
+    _need(k, torch.float16, (B, Hkv, n, D), "k")
+    _need(v, torch.float16, (B, Hkv, n, D), "v")
+    o = torch.empty_like(q) if o is None else o
+    col = torch.empty((B, Hkv, n), dtype=torch.float32, device=q.device) \
+        if col is None else col
+    sel = torch.empty((B, Hkv, n_hh + n_recent), dtype=torch.int32,
+                      device=q.device) if sel is None else sel
+    ws_bytes = 0
+    if lse is None and ws is None:
+        ws = torch.empty(prefill_ws_bytes(dims, n), dtype=torch.uint8,
+                         device=q.device)
+    if ws is not None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().minikv_prefill_select(
+        ctypes.byref(dims), n, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(col),
+        _ptr(lse), n_hh, n_recent, _ptr(sel), _ptr(ws), ws_bytes,
+        _stream(stream)))
+    return o, col, sel
+
+
+def pack(dims, k, v, sel, cache, stream=None):
+    B, Hkv, D = dims.batch, dims.n_kv_heads, dims.head_dim
+    n = k.shape[2]
+    _need(k, torch.float16, (B, Hkv, n, D), "k")
+    _need(v, torch.float16, (B, Hkv, n, D), "v")
+    n_sel = sel.shape[-1]
+    _need(sel, torch.int32, (B, Hkv, n_sel), "sel")
+    _check(lib().minikv_pack(ctypes.byref(dims), n, _ptr(k), _ptr(v),
+                             _ptr(sel), n_sel, ctypes.byref(cache.c),
+                             _stream(stream)))
+
+
+def append(dims, cache, k_new, v_new, stream=None):
+    shape = (dims.batch, dims.n_kv_heads, dims.head_dim)
+    _need(k_new, torch.float16, shape, "k_new")
+    _need(v_new, torch.float16, shape, "v_new")
+    _check(lib().minikv_append(ctypes.byref(dims), ctypes.byref(cache.c),
+                               _ptr(k_new), _ptr(v_new), _stream(stream)))
+
+
+def decode_attn(dims, cache, q, o=None, ws=None, stream=None):
+    shape = (dims.batch, dims.n_q_heads, dims.head_dim)
+    _need(q, torch.float16, shape, "q")
+    o = torch.empty_like(q) if o is None else o
+    if ws is None:
+        ws = torch.empty(decode_ws_bytes(dims, cache.capacity),
+                         dtype=torch.uint8, device=q.device)
+    _check(lib().minikv_decode_attn(ctypes.byref(dims), ctypes.byref(cache.c),
+                                    _ptr(q), _ptr(o), _ptr(ws),
+                                    ws.numel() * ws.element_size(),
+                                    _stream(stream)))
+    return o

@@ -239,20 +239,33 @@ class OracleCache:
         self.vz[b, h, at:at + mp] = out["vz"]
         return mp
 
-    def pack(self, k, v, sel):
-        """k, v [B][Hkv][n][D]; sel [B][Hkv][m] ascending."""
+    def pack(self, k, v, sel, units=None, workers=1):
+        """k, v [B][Hkv][n][D]; sel [B][Hkv][m] ascending.  `units` limits
+        the work to the listed (b, h) pairs (the others stay zero);
+        `workers` > 1 runs units on a thread pool (same arithmetic)."""
         k, v = _u16(k), _u16(v)
         sel = np.asarray(sel, np.int32)
         m = sel.shape[-1]
         mp = (m // self.Gk) * self.Gk
         if mp > self.cap or m - mp > self.nr:
             raise ValueError("capacity exceeded")
-        for b in range(self.B):
-            for h in range(self.Hkv):
-                out = pack_unit(k[b, h], v[b, h], sel[b, h], self.Gk, self.Gv)
-                self._store(b, h, 0, out)
-                self.kres[b, h, :m - mp] = out["kres"]
-                self.vres[b, h, :m - mp] = out["vres"]
+        if units is None:
+            units = [(b, h) for b in range(self.B) for h in range(self.Hkv)]
+
+        def one(bh):
+            b, h = bh
+            out = pack_unit(k[b, h], v[b, h], sel[b, h], self.Gk, self.Gv)
+            self._store(b, h, 0, out)
+            self.kres[b, h, :m - mp] = out["kres"]
+            self.vres[b, h, :m - mp] = out["vres"]
+
+        if workers > 1:
+            import concurrent.futures as cf
+            with cf.ThreadPoolExecutor(workers) as ex:
+                list(ex.map(one, units))
+        else:
+            for bh in units:
+                one(bh)
         self.n_packed, self.n_res = mp, m - mp
 
     def append(self, k_new, v_new):

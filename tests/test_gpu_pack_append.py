@@ -1,0 +1,151 @@
+"""GPU parity of minikv_pack and minikv_append against the oracle: every
+packed code word, fp16 scale/zero and residual row must be bit-identical."""
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantized_attention_two_amd import synth
+from gpu_util import assert_cache_equal, dev16, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _pack_case(torch, mk, B, Hkv, D, Gk, Gv, n, m, seed, cap=None,
+               k=None, v=None):
+    units = B * Hkv
+    if k is None:
+        k, v = synth.gen_kv(seed, units, n, D)
+    sel = synth.gen_selection(seed, units, n, m) if m < n else \
+        np.tile(np.arange(n, dtype=np.int32), (units, 1))
+    k = k.reshape(B, Hkv, n, D)
+    v = v.reshape(B, Hkv, n, D)
+    sel = sel.reshape(B, Hkv, m)
+    cap = cap if cap is not None else ((m // Gk) * Gk + 256 + Gk - 1) // Gk * Gk
+    dims = mk.make_dims(B, Hkv, Hkv, D, Gk, Gv)
+    say("pack", dict(B=B, Hkv=Hkv, D=D, Gk=Gk, Gv=Gv, n=n, m=m, seed=seed))
+    cache = mk.LayerCache(dims, cap)
+    mk.pack(dims, dev16(torch, k), dev16(torch, v),
+            torch.from_numpy(np.ascontiguousarray(sel)).cuda(), cache)
+    torch.cuda.synchronize()
+    oc = oracle.OracleCache(B, Hkv, D, Gk, Gv, cap)
+    oc.pack(k, v, sel)
+    assert_cache_equal(cache, oc, B, Hkv)
+    return dims, cache, oc, k, v
+
+
+@pytest.mark.parametrize("B,Hkv,D,Gk,Gv,n,m", [
+    (1, 4, 64, 32, 16, 256, 128),        # tiny single-layer workload shape
+    (2, 3, 128, 16, 16, 500, 237),       # ragged tail
+    (1, 2, 128, 16, 32, 300, 150),
+    (1, 2, 64, 64, 64, 400, 200),
+    (2, 1, 128, 128, 16, 640, 600),
+    (1, 3, 128, 16, 16, 100, 9),         # everything in the residual
+    (1, 2, 128, 16, 16, 64, 64),         # all tokens selected
+])
+def test_pack_random(B, Hkv, D, Gk, Gv, n, m):
+    torch, mk = require_gpu()
+    _pack_case(torch, mk, B, Hkv, D, Gk, Gv, n, m, seed=B * 1000 + n + m)
+
+
+def test_pack_empty_selection():
+    torch, mk = require_gpu()
+    dims = mk.make_dims(1, 2, 2, 128)
+    cache = mk.LayerCache(dims, 64)
+    k = torch.zeros((1, 2, 32, 128), dtype=torch.float16, device="cuda")
+    sel = torch.zeros((1, 2, 0), dtype=torch.int32, device="cuda")
+    mk.pack(dims, k, k, sel, cache)
+    assert (cache.n_packed, cache.n_res) == (0, 0)
+
+
+def _edge_tensor(D, n, r):
+    """fp16 [n][D] whose 16-element groups hit the codec's corner cases."""
+    x = r.standard_normal((n, D)).astype(np.float16)
+    flat = x.reshape(-1, 16)
+    kinds = [
+        lambda: np.full(16, 0.75),                               # constant
+        lambda: np.array([0, 3, 0.5, 1.5, 2.5] + [1] * 11),       # exact ties
+        lambda: np.array([-0.0, 0.0] * 8),                        # signed zeros
+        lambda: np.array([5.96e-8, 1.19e-7] * 8),                 # subnormal range
+        lambda: np.array([6e-8] + [0.0] * 15),                    # scale -> 0
+        lambda: np.array([-65504, 65504] + [0] * 14),             # full range
+        lambda: np.array([1024, 1025, 1026, 1027] * 4),           # step 1
+        lambda: r.standard_normal(16) * 1e-4 + 7.0,               # tiny spread
+    ]
+    for i in range(flat.shape[0]):
+        if i % 3 == 0:
+            flat[i] = np.asarray(kinds[(i // 3) % len(kinds)](),
+                                 np.float32).astype(np.float16)
+    return x
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_pack_codec_corner_cases(D):
+    torch, mk = require_gpu()
+    r = np.random.default_rng(D)
+    n = 256
+    # value groups run along channels, key groups along tokens
+    v = np.stack([_edge_tensor(D, n, r) for _ in range(2)])
+    k = np.stack([_edge_tensor(n, D, r).T.copy() for _ in range(2)])
+    _pack_case(torch, mk, 1, 2, D, 16, 16, n, n, seed=0, k=k, v=v)
+
+
+def test_pack_capacity_error_has_no_side_effect():
+    torch, mk = require_gpu()
+    dims = mk.make_dims(1, 2, 2, 128)
+    cache = mk.LayerCache(dims, 32)
+    k = torch.zeros((1, 2, 100, 128), dtype=torch.float16, device="cuda")
+    sel = torch.arange(50, dtype=torch.int32, device="cuda").repeat(1, 2, 1)
+    with pytest.raises(mk.MiniKVError) as e:
+        mk.pack(dims, k, k, sel, cache)
+    assert e.value.status == mk.ECAPACITY
+    assert (cache.n_packed, cache.n_res) == (0, 0)
+
+
+@pytest.mark.parametrize("Gk,nr,D,g", [(16, 128, 128, 1), (32, 128, 64, 1),
+                                       (16, 64, 128, 2)])
+def test_append_and_flush_bit_exact(Gk, nr, D, g):
+    torch, mk = require_gpu()
+    B, Hkv, n, m = 2, 2, 300, 100 + Gk // 2
+    units = B * Hkv
+    k, v = synth.gen_kv(77, units, n, D)
+    sel = synth.gen_selection(78, units, n, m)
+    k, v = k.reshape(B, Hkv, n, D), v.reshape(B, Hkv, n, D)
+    sel = sel.reshape(B, Hkv, m)
+    cap = (m // Gk) * Gk + 2 * nr
+    dims = mk.make_dims(B, Hkv, Hkv, D, Gk, 16, nr)
+    cache = mk.LayerCache(dims, cap)
+    say("append", dict(Gk=Gk, nr=nr, D=D, m=m, cap=cap))
+    mk.pack(dims, dev16(torch, k), dev16(torch, v),
+            torch.from_numpy(sel).cuda(), cache)
+    oc = oracle.OracleCache(B, Hkv, D, Gk, 16, cap, nr)
+    oc.pack(k, v, sel)
+    steps = 2 * nr - (m - (m // Gk) * Gk)        # through two flushes
+    for s in range(steps):
+        _, kn, vn = synth.gen_decode_step(9, 0, s, B, Hkv, Hkv, D)
+        mk.append(dims, cache, dev16(torch, kn), dev16(torch, vn))
+        oc.append(kn, vn)
+        if s % 17 == 0 or oc.n_res in (0, 1, nr - 1):
+            torch.cuda.synchronize()
+            assert_cache_equal(cache, oc, B, Hkv)
+    assert cache.n_packed == (m // Gk) * Gk + 2 * nr and cache.n_res == 0
+    torch.cuda.synchronize()
+    assert_cache_equal(cache, oc, B, Hkv)
+    # the next flush would overflow: error, and no counter moves
+    for s in range(nr - 1):
+        mk.append(dims, cache, dev16(torch, kn), dev16(torch, vn))
+    with pytest.raises(mk.MiniKVError) as e:
+        mk.append(dims, cache, dev16(torch, kn), dev16(torch, vn))
+    assert e.value.status == mk.ECAPACITY
+    assert cache.n_res == nr - 1
+
+
+def test_pack_full_size_llama2_7b_layers():
+    """The 4096-token, 32-head workload at its real per-layer selection sizes
+    (pyramid layer 0 and layer 31), every unit compared."""
+    torch, mk = require_gpu()
+    n, H, D = 4096, 32, 128
+    ks, r = oracle.budgets(n, 32, depth=7, pyramid=True)
+    for layer in (0, 31):
+        m = int(ks[layer]) + r
+        _pack_case(torch, mk, 1, H, D, 16, 16, n, m, seed=layer,
+                   cap=((m // 16) * 16 + 128 + 15) // 16 * 16)
