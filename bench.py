@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of the MiniKV-style compressed-KV path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input, layer by
+layer as a model runs it:
+  prefill: for every layer, minikv_prefill_select (pass 1: attention output
+           + LSE; pass 2: per-key cumulative scores; top-k + recent window)
+           and minikv_pack (INT2 keys/values, fp16 residual tail);
+  decode:  for every decode step and every layer, minikv_append (with the
+           residual flush every 128 tokens) and minikv_decode_attn.
+Inputs (prompt Q/K/V of every layer and the decode-step q/k/v) are resident
+in HBM before the timed region.
+
+Printed: one JSON line.  `value` is the decode phase's algorithmic bytes
+(packed codes + fp16 scale/zero + fp16 residual + q/o, counted as the method
+must move them) divided by the decode phase's wall time; the prefill phase's
+algorithmic TFLOP/s (3 D n (n+1) per query head and layer: QK^T and PV of
+pass 1, QK^T again in pass 2) is reported next to it.  `roofline` is for the
+decode-attention call, timed with HIP events on the stream it runs on.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_FP16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--config", type=int, default=2,
+                   help="workload id (configs.py); default: the 4096-token "
+                        "Llama2-7B-shaped stack")
+    p.add_argument("--distinct-layers", type=int, default=0,
+                   help="generate this many distinct layer inputs and cycle "
+                        "them (0 = all layers distinct)")
+    p.add_argument("--distinct-steps", type=int, default=0,
+                   help="distinct decode-step inputs to generate and cycle "
+                        "(0 = all)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="rough CPU budget of the oracle baseline")
+    return p.parse_args()
+
+
+def decode_bytes(c, n_packed, n_res):
+    """Algorithmic bytes of one decode-attention call (all units)."""
+    D, Gk, Gv = c["D"], c["Gk"], c["Gv"]
+    units = c["B"] * c["Hkv"]
+    per_unit = (n_packed * D // 4 * 2                      # K and V codes
+                + (n_packed // Gk) * D * 4                  # K scale+zero
+                + n_packed * (D // Gv) * 4                  # V scale+zero
+                + n_res * D * 4)                            # fp16 residual
+    return units * per_unit + c["B"] * c["Hq"] * D * 4      # + q and o
+
+
+def prefill_flops(c):
+    n, D = c["n"], c["D"]
+    return 3.0 * D * n * (n + 1) * c["B"] * c["Hq"]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              "path (each GPU would run the same kernels on its own share of "
+              "kv heads, with no exchange); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_quantized_attention_two_amd import configs, minikv, synth
+    minikv.lib()
+    assert torch.cuda.is_available(), "needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    c = configs.get(args.config)
+    B, Hq, Hkv, D, n, L = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"], c["L"]
+    Gk, Gv, nr, S = c["Gk"], c["Gv"], c["residual_cap"], c["decode_steps"]
+    ks, r = minikv.pyramid_budgets(n, L, c["hh"], c["rw"], c["depth"],
+                                   c["pyramid"])
+    dims = minikv.make_dims(B, Hq, Hkv, D, Gk, Gv, nr)
+    nl = args.distinct_layers or L
+    ns = args.distinct_steps or S
+
+    t0 = time.time()
+    qkv = [None] * nl
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
+        futs = {ex.submit(synth.gen_prefill, args.config, l): l
+                for l in range(nl)}
+        for f in cf.as_completed(futs):
+            qkv[futs[f]] = tuple(torch.from_numpy(a).to(dev) for a in f.result())
+    dq = torch.empty((ns, nl, B, Hq, D), dtype=torch.float16, device=dev)
+    dk = torch.empty((ns, nl, B, Hkv, D), dtype=torch.float16, device=dev)
+    dv = torch.empty_like(dk)
+    for s in range(ns):
+        for l in range(nl):
+            a, b_, c_ = synth.gen_decode_step(args.config, l, s, B, Hq, Hkv, D)
+            dq[s, l].copy_(torch.from_numpy(a))
+            dk[s, l].copy_(torch.from_numpy(b_))
+            dv[s, l].copy_(torch.from_numpy(c_))
+    gen_s = time.time() - t0
+
+    outs, caches, sels, cols = [], [], [], []
+    ws_pref = torch.empty(minikv.prefill_ws_bytes(dims, n), dtype=torch.uint8,
+                          device=dev)
+    for l in range(L):
+        m = ks[l] + r
+        cap = ((m // Gk) * Gk + S + nr + Gk - 1) // Gk * Gk
+        caches.append(minikv.LayerCache(dims, cap, dev))
+        outs.append(torch.empty((B, Hq, n, D), dtype=torch.float16, device=dev))
+        cols.append(torch.empty((B, Hkv, n), dtype=torch.float32, device=dev))
+        sels.append(torch.empty((B, Hkv, m), dtype=torch.int32, device=dev))
+    max_cap = max(x.capacity for x in caches)
+    ws_dec = torch.zeros(minikv.decode_ws_bytes(dims, max_cap),
+                         dtype=torch.uint8, device=dev)
+    od = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev_dec = []        # (start, end, bytes) of every timed decode call
+    ev_pre = []        # (start, end) of every timed prefill_select call
+
+    def one_step(record):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e2 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for l in range(L):
+            q, k, v = qkv[l % nl]
+            if record:
+                a = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            minikv.prefill_select(dims, q, k, v, ks[l], r, o=outs[l],
+                                  col=cols[l], sel=sels[l], ws=ws_pref)
+            if record:
+                b = torch.cuda.Event(enable_timing=True)
+                b.record(stream)
+                ev_pre.append((a, b))
+            minikv.pack(dims, k, v, sels[l], caches[l])
+        e1.record(stream)
+        dbytes = 0
+        for s in range(S):
+            for l in range(L):
+                cache = caches[l]
+                minikv.append(dims, cache, dk[s % ns, l % nl], dv[s % ns, l % nl])
+                nbytes = decode_bytes(c, cache.n_packed, cache.n_res)
+                dbytes += nbytes
+                if record:
+                    a = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                minikv.decode_attn(dims, cache, dq[s % ns, l % nl], o=od,
+                                   ws=ws_dec)
+                if record:
+                    b = torch.cuda.Event(enable_timing=True)
+                    b.record(stream)
+                    ev_dec.append((a, b, nbytes))
+        e2.record(stream)
+        return e0, e1, e2, dbytes
+
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+
+    phase = []
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        phase.append(one_step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    pre_ms = sum(e0.elapsed_time(e1) for e0, e1, _, _ in phase)
+    dec_ms = sum(e1.elapsed_time(e2) for _, e1, e2, _ in phase)
+    dec_bytes = sum(x[3] for x in phase)
+    value = dec_bytes / (dec_ms * 1e-3) / 1e9
+    pre_tflops = prefill_flops(c) * L * args.steps / (pre_ms * 1e-3) / 1e12
+    ms_per_step = wall * 1e3 / args.steps
+
+    dec_call_ms = np.array([a.elapsed_time(b) for a, b, _ in ev_dec])
+    dec_call_bytes = np.array([x[2] for x in ev_dec], np.float64)
+    avg_dec_ms = float(dec_call_ms.mean())
+    avg_dec_bytes = float(dec_call_bytes.mean())
+    achieved = avg_dec_bytes / (avg_dec_ms * 1e-3) / 1e9
+    pre_call_ms = np.array([a.elapsed_time(b) for a, b in ev_pre])
+    pre_achieved = prefill_flops(c) / (pre_call_ms.mean() * 1e-3) / 1e12
+
+    result = {
+        "metric": "packed-KV decode attention GB/s (% HBM peak) + prefill "
+                  "selective-attn TFLOP/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 in, fp32 accumulate; int2 packed cache",
+        "data": "synthetic (seeded N(0,1) Q/K/V with attention sink, planted "
+                "heavy hitters and key outlier channels)",
+        "config": {
+            "workload": c["name"], "config_id": args.config, "batch": B,
+            "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D,
+            "prompt_len": n, "layers": L, "decode_steps": S,
+            "budget": "pyramid d=%d" % c["depth"] if c["pyramid"] else
+                      "uniform", "hh_frac": "1/4", "recent_frac": "1/4",
+            "group_k": Gk, "group_v": Gv, "residual_cap": nr,
+            "distinct_layer_inputs": nl, "distinct_decode_inputs": ns,
+            "parallelism": "single GPU",
+        },
+        "decode_pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "prefill_tflops": round(pre_tflops, 2),
+        "prefill_pct_mfma_fp16_peak": round(100 * pre_tflops /
+                                            MFMA_FP16_PEAK_TFLOPS, 2),
+        "phase_ms_per_step": {"prefill": round(pre_ms / args.steps, 3),
+                              "decode": round(dec_ms / args.steps, 3)},
+        "roofline": {
+            "kernel": "minikv_decode_attn (split-KV decode + combine)",
+            "bound": "hbm", "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "avg_launch_us": round(avg_dec_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(avg_dec_bytes),
+            "launches": int(dec_call_ms.size),
+        },
+        "roofline_prefill": {
+            "kernel": "minikv_prefill_select (pass 1 + pass 2 + select)",
+            "bound": "mfma", "achieved": round(pre_achieved, 2),
+            "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(pre_achieved / MFMA_FP16_PEAK_TFLOPS, 4),
+            "avg_launch_us": round(float(pre_call_ms.mean()) * 1e3, 3),
+            "algorithmic_flops_per_launch": prefill_flops(c),
+        },
+        "input_generation_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, c, ks, r, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, c, ks, r, budget_s):
+    """The oracle, as it is, on host threads: decode attention of sampled
+    units of layer 0 (packed by the oracle itself from the same seeded
+    inputs), reported in the metric's unit, plus the oracle's prefill rate on
+    one unit for context."""
+    import concurrent.futures as cf
+
+    import oracle
+    from bit_quantized_attention_two_amd import synth
+    oracle.build(force=False)
+    cores = min(16, os.cpu_count() or 1)
+    B, Hq, Hkv, D, n = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"]
+    g = Hq // Hkv
+    m = ks[0] + r
+    q, k, v = synth.gen_prefill(args.config, 0, batches=[0])
+    units = [(0, h) for h in range(Hkv)]
+    cap = ((m // c["Gk"]) * c["Gk"] + 256)
+    oc = oracle.OracleCache(1, Hkv, D, c["Gk"], c["Gv"], cap,
+                            c["residual_cap"])
+    # heavy hitters: the oracle's own prefill scores would cost O(n^2) per
+    # unit; use its selection on the first unit's scores for every unit
+    t0 = time.perf_counter()
+    _, _, col = oracle.prefill_unit(q[0, :g], k[0, 0], v[0, 0])
+    t_pref = time.perf_counter() - t0
+    sel0 = oracle.select(col, ks[0], r)
+    sel = np.tile(sel0, (1, Hkv, 1))
+    t0 = time.perf_counter()
+    oc.pack(k, v, sel, workers=cores)
+    t_pack = time.perf_counter() - t0
+    qd, _, _ = synth.gen_decode_step(args.config, 0, 0, 1, Hq, Hkv, D)
+    nbytes_call = decode_bytes(dict(c, B=1), oc.n_packed, oc.n_res)
+    reps = 0
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(cores) as ex:
+        while True:
+            list(ex.map(lambda u: oc.decode_unit(qd[0, u[1] * g:(u[1] + 1) * g],
+                                                 0, u[1]), units))
+            reps += 1
+            if time.perf_counter() - t0 > budget_s / 2 or reps >= 10000:
+                break
+    t_dec = time.perf_counter() - t0
+    return {
+        "value": round(nbytes_call * reps / t_dec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "decode attention of all %d kv-head units of layer 0, batch "
+                  "element 0 (%d packed + %d residual tokens each), repeated "
+                  "%d times on %d threads; fp64 oracle" %
+                  (Hkv, oc.n_packed, oc.n_res, reps, cores),
+        "prefill_tflops_one_unit_one_thread": round(
+            prefill_flops(dict(c, B=1, Hq=g)) / t_pref / 1e12, 6),
+        "pack_s_all_units": round(t_pack, 3),
+        "seconds": round(t_dec + t_pref + t_pack, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()
