@@ -49,6 +49,9 @@ def parse():
                    help="distinct decode-step inputs to generate and cycle "
                         "(0 = all)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eager", action="store_true",
+                   help="launch every call from Python instead of replaying "
+                        "the captured HIP graphs of a step")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="rough CPU budget of the oracle baseline")
     return p.parse_args()
@@ -130,56 +133,98 @@ def main():
     od = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     stream = torch.cuda.current_stream()
 
-    ev_dec = []        # (start, end, bytes) of every timed decode call
-    ev_pre = []        # (start, end) of every timed prefill_select call
+    # One step in model order.  The prefill part runs every layer's
+    # prefill+select and pack; the decode part runs, for every decode step,
+    # every layer's append and decode attention.
+    dec_bytes_per_call = []
 
-    def one_step(record):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e2 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+    def prefill_part():
         for l in range(L):
             q, k, v = qkv[l % nl]
-            if record:
-                a = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
             minikv.prefill_select(dims, q, k, v, ks[l], r, o=outs[l],
                                   col=cols[l], sel=sels[l], ws=ws_pref)
-            if record:
-                b = torch.cuda.Event(enable_timing=True)
-                b.record(stream)
-                ev_pre.append((a, b))
             minikv.pack(dims, k, v, sels[l], caches[l])
-        e1.record(stream)
-        dbytes = 0
+
+    def decode_part():
+        dec_bytes_per_call.clear()
         for s in range(S):
             for l in range(L):
                 cache = caches[l]
                 minikv.append(dims, cache, dk[s % ns, l % nl], dv[s % ns, l % nl])
-                nbytes = decode_bytes(c, cache.n_packed, cache.n_res)
-                dbytes += nbytes
-                if record:
-                    a = torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
+                dec_bytes_per_call.append(decode_bytes(c, cache.n_packed,
+                                                       cache.n_res))
                 minikv.decode_attn(dims, cache, dq[s % ns, l % nl], o=od,
                                    ws=ws_dec)
-                if record:
-                    b = torch.cuda.Event(enable_timing=True)
-                    b.record(stream)
-                    ev_dec.append((a, b, nbytes))
-        e2.record(stream)
-        return e0, e1, e2, dbytes
 
-    for _ in range(args.warmup):
-        one_step(False)
+    def capture(fn, side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            fn()
+        return g
+
+    # warm-up (eager), then capture one step as two graphs
+    for _ in range(max(1, args.warmup)):
+        prefill_part()
+        decode_part()
     torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    graphs = None
+    if not args.eager:
+        side.wait_stream(stream)
+        graphs = (capture(prefill_part, side), capture(decode_part, side))
+        stream.wait_stream(side)
+        for _ in range(args.warmup):
+            graphs[0].replay()
+            graphs[1].replay()
+        torch.cuda.synchronize()
 
     phase = []
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        phase.append(one_step(True))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e2 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graphs[0].replay() if graphs else prefill_part()
+        e1.record(stream)
+        graphs[1].replay() if graphs else decode_part()
+        e2.record(stream)
+        phase.append((e0, e1, e2, sum(dec_bytes_per_call)))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+
+    # Per-call durations of the two dominant calls, measured right after the
+    # timed steps on the same stream with HIP events: the decode-attention
+    # call of every layer, in its end-of-step cache state, replayed
+    # back-to-back from a graph (R rounds of all layers), and each layer's
+    # prefill+select call between its own events.
+    R = 8
+    side.wait_stream(stream)
+    g_kern = capture(lambda: [minikv.decode_attn(dims, caches[l],
+                                                 dq[0, l % nl], o=od,
+                                                 ws=ws_dec)
+                              for _ in range(R) for l in range(L)], side)
+    stream.wait_stream(side)
+    g_kern.replay()
+    ka, kb = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    ka.record(stream)
+    g_kern.replay()
+    kb.record(stream)
+    torch.cuda.synchronize()
+    dec_call_ms = np.array([ka.elapsed_time(kb) / (R * L)])
+    dec_call_bytes = np.array([decode_bytes(c, x.n_packed, x.n_res)
+                               for x in caches], np.float64)
+    pre_call_ms = []
+    for l in range(L):
+        q, k, v = qkv[l % nl]
+        a, b = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        a.record(stream)
+        minikv.prefill_select(dims, q, k, v, ks[l], r, o=outs[l], col=cols[l],
+                              sel=sels[l], ws=ws_pref)
+        b.record(stream)
+        pre_call_ms.append((a, b))
+    torch.cuda.synchronize()
+    pre_call_ms = [a.elapsed_time(b) for a, b in pre_call_ms]
 
     pre_ms = sum(e0.elapsed_time(e1) for e0, e1, _, _ in phase)
     dec_ms = sum(e1.elapsed_time(e2) for _, e1, e2, _ in phase)
@@ -188,12 +233,10 @@ def main():
     pre_tflops = prefill_flops(c) * L * args.steps / (pre_ms * 1e-3) / 1e12
     ms_per_step = wall * 1e3 / args.steps
 
-    dec_call_ms = np.array([a.elapsed_time(b) for a, b, _ in ev_dec])
-    dec_call_bytes = np.array([x[2] for x in ev_dec], np.float64)
     avg_dec_ms = float(dec_call_ms.mean())
     avg_dec_bytes = float(dec_call_bytes.mean())
     achieved = avg_dec_bytes / (avg_dec_ms * 1e-3) / 1e9
-    pre_call_ms = np.array([a.elapsed_time(b) for a, b in ev_pre])
+    pre_call_ms = np.array(pre_call_ms)
     pre_achieved = prefill_flops(c) / (pre_call_ms.mean() * 1e-3) / 1e12
 
     result = {
@@ -220,6 +263,8 @@ def main():
             "group_k": Gk, "group_v": Gv, "residual_cap": nr,
             "distinct_layer_inputs": nl, "distinct_decode_inputs": ns,
             "parallelism": "single GPU",
+            "launch": "eager" if args.eager else
+                      "HIP graphs (one step captured, replayed per step)",
         },
         "decode_pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "prefill_tflops": round(pre_tflops, 2),
@@ -228,13 +273,14 @@ def main():
         "phase_ms_per_step": {"prefill": round(pre_ms / args.steps, 3),
                               "decode": round(dec_ms / args.steps, 3)},
         "roofline": {
-            "kernel": "minikv_decode_attn (split-KV decode + combine)",
+            "kernel": "minikv_decode_attn (split-KV decode + combine "
+                      "kernels), all layers, end-of-step cache state",
             "bound": "hbm", "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
             "avg_launch_us": round(avg_dec_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": int(avg_dec_bytes),
-            "launches": int(dec_call_ms.size),
+            "launches": R * L,
         },
         "roofline_prefill": {
             "kernel": "minikv_prefill_select (pass 1 + pass 2 + select)",

@@ -427,6 +427,9 @@ int32_t minikv_decode_attn(const minikv_dims *d, const minikv_layer_cache *c,
     if (c->n_packed + c->n_res == 0) return fail(MINIKV_EINVAL, "cache holds no token");
     const int units = d->batch * d->n_kv_heads;
     const int g = d->n_q_heads / d->n_kv_heads;
+    if (c->capacity > minikv::decode_max_capacity(g))
+        return fail(MINIKV_EUNSUPPORTED, "capacity %d above the decode limit %d",
+                    c->capacity, minikv::decode_max_capacity(g));
     const size_t need = minikv::decode_ws_bytes(units, g, d->head_dim, c->capacity);
     if (ws_bytes < need)
         return fail(MINIKV_EINVAL, "workspace too small: %zu < %zu", ws_bytes, need);

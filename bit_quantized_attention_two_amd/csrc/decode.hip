@@ -12,12 +12,24 @@
 //
 // with q' = q log2(e) / sqrt(D) so that the softmax uses exp2.  The products
 // q' s (per key group and channel) and p s (per token and channel group) are
-// formed once and reused for the 16 codes of a word.
+// formed once and reused for the 16 codes of a word; all g query heads of a
+// kv head share each read of its codes.
 //
-// Split-KV: block (chunk, unit) handles CH packed tokens of one unit (all g
-// query heads share each read of the unit's codes); one extra block per unit
-// handles the residual.  Each block writes (max, sum, unnormalised o) per
-// head and a combine kernel merges the splits.
+// Work split: block (split, unit) covers `chunk` packed tokens of one unit,
+// each of its 4 waves a quarter of them; the last split of a unit is its
+// fp16 residual when it has one.  A wave computes its logits (the 16 lanes
+// of a 16-token key row split the channels), its own softmax statistics and
+// its P.V; the block merges its waves in LDS and writes one partial
+// (max, sum, unnormalised o) to the workspace.  A second kernel merges the
+// partials of each (unit, head) and writes o.  (Merging in the last block to
+// finish would need device-scope fences, which on this multi-die part write
+// back and invalidate the L2 of every block that takes them.)
+//
+// Global loads are issued ahead of their use -- the next 16-token key row
+// while the current one is reduced, four value rows at a time -- so that
+// each wave keeps several HBM round trips in flight.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -25,16 +37,19 @@ namespace minikv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxChunk = 1024;
-constexpr int kMinChunk = 256;
+constexpr int kWaves = 4;
+constexpr int kMinWaveChunk = 64;
+constexpr int kMaxWaveChunk = 512;
+constexpr int kMaxSplit = 512;            // LDS rows of the combine kernel
 
 struct DecArgs {
     const uint16_t *q;
+    uint16_t *o;
     CacheView c;
     int n_packed, n_res, chunk, n_chunks, nsplit;
     float qscale;
-    float *part_ml;   // [units][nsplit][G][2]
-    float *part_o;    // [units][nsplit][G][D]
+    float *part_ml;     // [units][nsplit][G][2]
+    float *part_o;      // [units][nsplit][G][D]
 };
 
 template <int CTRL>
@@ -43,12 +58,55 @@ __device__ __forceinline__ float dpp(float v) {
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                            CTRL, 0xf, 0xf, false));
 }
-// lane ^ 1 and lane ^ 2 inside a quad (DPP quad_perm).
-__device__ __forceinline__ float xor1(float v) { return dpp<0xB1>(v); }
-__device__ __forceinline__ float xor2(float v) { return dpp<0x4E>(v); }
+// Sum over the 16 lanes of a DPP row; every lane receives the total.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<0x128>(v);       // row_ror:8
+    v += dpp<0x124>(v);       // row_ror:4
+    v += dpp<0x122>(v);       // row_ror:2
+    v += dpp<0x121>(v);       // row_ror:1
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, shfl_xor(v, off));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int off = 32; off > 0; off >>= 1) v += shfl_xor(v, off);
+    return v;
+}
+__device__ __forceinline__ void unpack8h(uint4 x, float *f) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = h2f((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
+}
+// N consecutive fp16 values (N = 4 or 8) -> fp32.
+template <int N>
+__device__ __forceinline__ void load_halves(const uint16_t *p, float *f) {
+    if constexpr (N == 8) {
+        unpack8h(*reinterpret_cast<const uint4 *>(p), f);
+    } else {
+        const uint2 x = *reinterpret_cast<const uint2 *>(p);
+        const uint32_t w[2] = {x.x, x.y};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = h2f((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
+    }
+}
+// N consecutive 32-bit words (N = 4 or 8).
+template <int N>
+__device__ __forceinline__ void load_words(const uint32_t *p, uint32_t *w) {
+    const uint4 a = reinterpret_cast<const uint4 *>(p)[0];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    if constexpr (N == 8) {
+        const uint4 b = reinterpret_cast<const uint4 *>(p)[1];
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+}
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
+    constexpr int WPT = D / 16;               // value words per token
+    constexpr int TS = 64 / WPT;              // tokens per V pass of a wave
+    constexpr int MAXW = kMaxWaveChunk * G <= 1024 ? kMaxWaveChunk : 1024 / G;
     const int unit = blockIdx.y;
     const int split = blockIdx.x;
     const int tid = threadIdx.x;
@@ -56,72 +114,87 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     const int wave = tid >> 6;
     const CacheView &c = a.c;
 
-    __shared__ float q_s[D * G];                // [c][h], pre-scaled
-    __shared__ float p_s[kMaxChunk * G];        // logits, then probabilities
-    __shared__ float red_s[4 * G * D];          // per-wave partial outputs
-    __shared__ float stat_s[4 * G];
-    __shared__ float m_s[G], l_s[G];
-
-    for (int i = tid; i < G * D; i += kThreads) {
-        const int h = i / D, ch = i % D;
-        q_s[ch * G + h] =
-            h2f(a.q[((size_t)unit * G + h) * D + ch]) * a.qscale;
-    }
-    __syncthreads();
+    __shared__ float p_s[kWaves][MAXW * G];   // logits, then probabilities
+    __shared__ float red_o[kWaves][G * D];
+    __shared__ float red_ml[kWaves][G][2];
+    __shared__ float mrg[G][2];
 
     const bool resid = split >= a.n_chunks;
-    const int tok0 = resid ? 0 : split * a.chunk;
-    const int nt = resid ? a.n_res : min(a.chunk, a.n_packed - tok0);
-
-    // ------------------------------------------------------------ logits
+    const int wchunk = a.chunk / kWaves;
+    int t0, nt;                               // this wave's tokens
     if (!resid) {
-        constexpr int TPR = D / 32;             // threads per 16-token row
-        constexpr int RPP = kThreads / TPR;
-        const int part = tid % TPR;
-        const int nrows = nt >> 4;
+        t0 = split * a.chunk + wave * wchunk;
+        nt = max(0, min(wchunk, a.n_packed - t0));
+    } else {
+        const int per = (a.n_res + kWaves - 1) / kWaves;
+        t0 = wave * per;
+        nt = max(0, min(per, a.n_res - t0));
+    }
+    const uint16_t *qu = a.q + (size_t)unit * G * D;
+    float *ps = p_s[wave];
+
+    // --------------------------------------------------------- logits
+    float m_w[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) m_w[h] = -INFINITY;
+    if (!resid) {
+        constexpr int CPL = D / 16;           // channels per lane
+        const int part = lane & 15;           // channels CPL part .. + CPL-1
+        const int rsub = lane >> 4;           // row of the 4-row pass
+        float qv[CPL][G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float f[CPL];
+            load_halves<CPL>(qu + h * D + CPL * part, f);
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) qv[i][h] = f[i] * a.qscale;
+        }
         const uint32_t *kq = reinterpret_cast<const uint32_t *>(c.kq) +
                              (size_t)unit * c.kq_unit();
         const uint16_t *ks = c.ks + (size_t)unit * c.km_unit();
         const uint16_t *kz = c.kz + (size_t)unit * c.km_unit();
-        for (int row = tid / TPR; row < nrows; row += RPP) {
-            const int wrow = (tok0 >> 4) + row;
+        const int nrows = nt >> 4;
+        // row r0 + rsub of each 4-row pass; the next pass's data is loaded
+        // before the current one is used
+        uint32_t wds[CPL];
+        float sv[CPL], zv[CPL];
+        auto load_row = [&](int row, uint32_t *w, float *sp, float *zp) {
+            const int wrow = (t0 >> 4) + row;
             const int grp = (wrow << 4) / c.Gk;
-            const uint32_t *kw = kq + (size_t)wrow * D;
-            const uint16_t *ksr = ks + (size_t)grp * D;
-            const uint16_t *kzr = kz + (size_t)grp * D;
-            float acc[16][G];
-            float bias[G];
+            load_words<CPL>(kq + (size_t)wrow * D + CPL * part, w);
+            load_halves<CPL>(ks + (size_t)grp * D + CPL * part, sp);
+            load_halves<CPL>(kz + (size_t)grp * D + CPL * part, zp);
+        };
+        // loads are never predicated off: a row past the end re-reads the
+        // last row and its result is discarded, so the loads of the next
+        // pass are in flight while this one computes
+        if (nrows > 0) load_row(min(rsub, nrows - 1), wds, sv, zv);
+        for (int r0 = 0; r0 < nrows; r0 += 4) {
+            const int row = r0 + rsub;
+            uint32_t nwds[CPL];
+            float nsv[CPL], nzv[CPL];
+            load_row(min(row + 4, nrows - 1), nwds, nsv, nzv);
+            if (row < nrows) {
+                float acc[16][G];
+                float bias[G];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                bias[h] = 0.f;
+                for (int h = 0; h < G; ++h) {
+                    bias[h] = 0.f;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) acc[t][h] = 0.f;
-            }
+                    for (int t = 0; t < 16; ++t) acc[t][h] = 0.f;
+                }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int cq = part + TPR * i;  // channels 4cq .. 4cq+3
-                const uint4 wq = *reinterpret_cast<const uint4 *>(kw + 4 * cq);
-                const uint2 sq = *reinterpret_cast<const uint2 *>(ksr + 4 * cq);
-                const uint2 zq = *reinterpret_cast<const uint2 *>(kzr + 4 * cq);
-                const uint32_t wds[4] = {wq.x, wq.y, wq.z, wq.w};
-                const float sv[4] = {h2f(sq.x & 0xffff), h2f(sq.x >> 16),
-                                     h2f(sq.y & 0xffff), h2f(sq.y >> 16)};
-                const float zv[4] = {h2f(zq.x & 0xffff), h2f(zq.x >> 16),
-                                     h2f(zq.y & 0xffff), h2f(zq.y >> 16)};
-#pragma unroll
-                for (int ch = 0; ch < 4; ++ch) {
+                for (int ch = 0; ch < CPL; ++ch) {
                     float W[G];
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        const float qv = q_s[(4 * cq + ch) * G + h];
-                        W[h] = qv * sv[ch];
-                        bias[h] += qv * zv[ch];
+                        W[h] = qv[ch][h] * sv[ch];
+                        bias[h] += qv[ch][h] * zv[ch];
                     }
-                    const uint32_t wd = wds[ch];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        // bytes of m hold the codes of tokens k, 4+k, 8+k, 12+k
-                        const uint32_t m = (wd >> (2 * k)) & 0x03030303u;
+                        // bytes of m: codes of tokens k, 4+k, 8+k, 12+k
+                        const uint32_t m = (wds[ch] >> (2 * k)) & 0x03030303u;
                         const float c0 = (float)(m & 0xff);
                         const float c1 = (float)((m >> 8) & 0xff);
                         const float c2 = (float)((m >> 16) & 0xff);
@@ -135,102 +208,88 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                         }
                     }
                 }
-            }
+                // lane `part` keeps token `part` of the row
+                float mine[G];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+                for (int h = 0; h < G; ++h) mine[h] = 0.f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const float v = row16_sum(acc[t][h] + bias[h]);
+                        if (t == part) mine[h] = v;
+                    }
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    float v = acc[t][h] + bias[h];
-                    v += xor1(v);
-                    if (TPR == 4) v += xor2(v);
-                    if ((t % TPR) == part) p_s[(row * 16 + t) * G + h] = v;
+                    ps[(row * 16 + part) * G + h] = mine[h];
+                    m_w[h] = fmaxf(m_w[h], mine[h]);
                 }
+            }
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                wds[i] = nwds[i];
+                sv[i] = nsv[i];
+                zv[i] = nzv[i];
             }
         }
     } else {
-        // residual: one thread per token, fp16 keys
         const uint16_t *kr = c.kres + (size_t)unit * c.res_unit();
-        for (int t = tid; t < nt; t += kThreads) {
+        for (int t = lane; t < nt; t += 64) {
             float acc[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) acc[h] = 0.f;
-            const uint4 *row = reinterpret_cast<const uint4 *>(kr + (size_t)t * D);
-#pragma unroll 4
+            const uint4 *row = reinterpret_cast<const uint4 *>(kr + (size_t)(t0 + t) * D);
+#pragma unroll 2
             for (int i = 0; i < D / 8; ++i) {
-                const uint4 x = row[i];
-                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                float kf[8];
+                unpack8h(row[i], kf);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float kv = h2f((uint16_t)(w[j >> 1] >> (16 * (j & 1))));
+                for (int h = 0; h < G; ++h) {
+                    float qf[8];
+                    unpack8h(*reinterpret_cast<const uint4 *>(qu + h * D + 8 * i), qf);
 #pragma unroll
-                    for (int h = 0; h < G; ++h)
-                        acc[h] += q_s[(8 * i + j) * G + h] * kv;
+                    for (int j = 0; j < 8; ++j) acc[h] += qf[j] * kf[j];
                 }
             }
 #pragma unroll
-            for (int h = 0; h < G; ++h) p_s[t * G + h] = acc[h];
-        }
-    }
-    __syncthreads();
-
-    // ----------------------------------------------------------- softmax
-    {
-        float mloc[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
-        for (int t = tid; t < nt; t += kThreads)
-#pragma unroll
-            for (int h = 0; h < G; ++h) mloc[h] = fmaxf(mloc[h], p_s[t * G + h]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            for (int off = 32; off > 0; off >>= 1)
-                mloc[h] = fmaxf(mloc[h], shfl_xor(mloc[h], off));
-            if (lane == 0) stat_s[wave * G + h] = mloc[h];
-        }
-        __syncthreads();
-        if (tid < G)
-            m_s[tid] = fmaxf(fmaxf(stat_s[tid], stat_s[G + tid]),
-                             fmaxf(stat_s[2 * G + tid], stat_s[3 * G + tid]));
-        __syncthreads();
-        float lloc[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) lloc[h] = 0.f;
-        for (int t = tid; t < nt; t += kThreads)
-#pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float p = exp2f(p_s[t * G + h] - m_s[h]);
-                p_s[t * G + h] = p;
-                lloc[h] += p;
+                const float v = acc[h] * a.qscale;
+                ps[t * G + h] = v;
+                m_w[h] = fmaxf(m_w[h], v);
             }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            for (int off = 32; off > 0; off >>= 1)
-                lloc[h] += shfl_xor(lloc[h], off);
         }
-        __syncthreads();                        // stat_s reuse
-        if (lane == 0)
-#pragma unroll
-            for (int h = 0; h < G; ++h) stat_s[wave * G + h] = lloc[h];
-        __syncthreads();
-        if (tid < G)
-            l_s[tid] = (stat_s[tid] + stat_s[G + tid]) +
-                       (stat_s[2 * G + tid] + stat_s[3 * G + tid]);
     }
 
-    // --------------------------------------------------------- P . V
+    // ------------------------------------------------ wave softmax stats
+    float l_w[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) m_w[h] = wave_max(m_w[h]);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int h = 0; h < G; ++h) l_w[h] = 0.f;
+    for (int t = lane; t < nt; t += 64)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float p = exp2f(ps[t * G + h] - m_w[h]);
+            ps[t * G + h] = p;
+            l_w[h] += p;
+        }
+#pragma unroll
+    for (int h = 0; h < G; ++h) l_w[h] = wave_sum(l_w[h]);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    // ----------------------------------------------------------- P . V
     if (!resid) {
-        constexpr int WPT = D / 16;             // value words per token
-        constexpr int TS = kThreads / WPT;
-        const int j = tid % WPT;
-        const int ts = tid / WPT;
+        const int j = lane % WPT;             // channels 16 j .. 16 j + 15
+        const int ts = lane / WPT;
         const int gpt = D / c.Gv;
         const int gsel = (j * 16) / c.Gv;
         const uint32_t *vw = reinterpret_cast<const uint32_t *>(c.vq) +
-                             (size_t)unit * c.vq_unit() + (size_t)tok0 * WPT + j;
-        const uint16_t *vsr = c.vs + (size_t)unit * c.vm_unit() +
-                              (size_t)tok0 * gpt + gsel;
-        const uint16_t *vzr = c.vz + (size_t)unit * c.vm_unit() +
-                              (size_t)tok0 * gpt + gsel;
+                             (size_t)unit * c.vq_unit() + (size_t)t0 * WPT + j;
+        const uint16_t *vsr = c.vs + (size_t)unit * c.vm_unit() + (size_t)t0 * gpt + gsel;
+        const uint16_t *vzr = c.vz + (size_t)unit * c.vm_unit() + (size_t)t0 * gpt + gsel;
         float acc[G][16];
         float zs[G];
 #pragma unroll
@@ -239,31 +298,49 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
         }
-        for (int t = ts; t < nt; t += TS) {
-            const uint32_t wd = vw[(size_t)t * WPT];
-            const float s = h2f(vsr[(size_t)t * gpt]);
-            const float z = h2f(vzr[(size_t)t * gpt]);
-            float ps[G];
+        constexpr int VB = 4;                 // value rows loaded per batch
+        for (int tb = ts; tb < nt; tb += VB * TS) {
+            // unpredicated loads (indices clamped to the last token; the
+            // extra rows get p = 0), all issued before the first use
+            uint32_t wdb[VB];
+            uint16_t sb[VB], zb[VB];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float p = p_s[t * G + h];
-                ps[h] = p * s;
-                zs[h] += p * z;
+            for (int i = 0; i < VB; ++i) {
+                const int t = min(tb + i * TS, nt - 1);
+                wdb[i] = vw[(size_t)t * WPT];
+                sb[i] = vsr[(size_t)t * gpt];
+                zb[i] = vzr[(size_t)t * gpt];
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                // bytes of m hold the codes of channels k, 4+k, 8+k, 12+k
-                const uint32_t m = (wd >> (2 * k)) & 0x03030303u;
-                const float c0 = (float)(m & 0xff);
-                const float c1 = (float)((m >> 8) & 0xff);
-                const float c2 = (float)((m >> 16) & 0xff);
-                const float c3 = (float)(m >> 24);
+            for (int i = 0; i < VB; ++i) {
+                const int t = tb + i * TS;
+                const bool ok = t < nt;
+                const int tc = min(t, nt - 1);
+                const float s = h2f(sb[i]);
+                const float z = h2f(zb[i]);
+                const uint32_t wd = wdb[i];
+                float pss[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    acc[h][k] += ps[h] * c0;
-                    acc[h][4 + k] += ps[h] * c1;
-                    acc[h][8 + k] += ps[h] * c2;
-                    acc[h][12 + k] += ps[h] * c3;
+                    const float p = ok ? ps[tc * G + h] : 0.f;
+                    pss[h] = p * s;
+                    zs[h] += p * z;
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    // bytes of m: codes of channels k, 4+k, 8+k, 12+k
+                    const uint32_t m = (wd >> (2 * k)) & 0x03030303u;
+                    const float c0 = (float)(m & 0xff);
+                    const float c1 = (float)((m >> 8) & 0xff);
+                    const float c2 = (float)((m >> 16) & 0xff);
+                    const float c3 = (float)(m >> 24);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        acc[h][k] += pss[h] * c0;
+                        acc[h][4 + k] += pss[h] * c1;
+                        acc[h][8 + k] += pss[h] * c2;
+                        acc[h][12 + k] += pss[h] * c3;
+                    }
                 }
             }
         }
@@ -279,28 +356,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    red_s[(wave * G + h) * D + j * 16 + e] = acc[h][e];
+                for (int e = 0; e < 16; ++e) red_o[wave][h * D + j * 16 + e] = acc[h][e];
     } else {
-        constexpr int CPT = D / 8;              // uint4 per residual row
-        constexpr int TS = kThreads / CPT;
-        const int c8 = tid % CPT;
-        const int ts = tid / CPT;
+        constexpr int CPT = D / 8;            // uint4 per residual row
+        constexpr int RTS = 64 / CPT;
+        const int c8 = lane % CPT;
+        const int ts = lane / CPT;
         const uint16_t *vr = c.vres + (size_t)unit * c.res_unit();
         float acc[G][8];
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        for (int t = ts; t < nt; t += TS) {
-            const uint4 x = reinterpret_cast<const uint4 *>(vr + (size_t)t * D)[c8];
-            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        for (int t = ts; t < nt; t += RTS) {
+            float vf[8];
+            unpack8h(reinterpret_cast<const uint4 *>(vr + (size_t)(t0 + t) * D)[c8], vf);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float p = p_s[t * G + h];
+                const float p = ps[t * G + h];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[h][e] += p * h2f((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+                for (int e = 0; e < 8; ++e) acc[h][e] += p * vf[e];
             }
         }
 #pragma unroll
@@ -315,69 +390,147 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    red_s[(wave * G + h) * D + c8 * 8 + e] = acc[h][e];
+                for (int e = 0; e < 8; ++e) red_o[wave][h * D + c8 * 8 + e] = acc[h][e];
     }
+    if (lane == 0)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            red_ml[wave][h][0] = m_w[h];
+            red_ml[wave][h][1] = l_w[h];
+        }
     __syncthreads();
 
+    // ----------------------------------------- merge the 4 waves, store
+    if (tid < G) {
+        float M = -INFINITY;
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][tid][0]);
+        float L = 0.f;
+        for (int w = 0; w < kWaves; ++w)
+            if (red_ml[w][tid][1] > 0.f) L += red_ml[w][tid][1] * exp2f(red_ml[w][tid][0] - M);
+        mrg[tid][0] = M;
+        mrg[tid][1] = L;
+    }
+    __syncthreads();
     const size_t sbase = (size_t)unit * a.nsplit + split;
     for (int i = tid; i < G * D; i += kThreads) {
-        const int h = i / D, ch = i % D;
-        const float v = (red_s[(0 * G + h) * D + ch] + red_s[(1 * G + h) * D + ch]) +
-                        (red_s[(2 * G + h) * D + ch] + red_s[(3 * G + h) * D + ch]);
-        a.part_o[(sbase * G + h) * D + ch] = v;
+        const int h = i / D;
+        const float M = mrg[h][0];
+        float v = 0.f;
+        for (int w = 0; w < kWaves; ++w)
+            if (red_ml[w][h][1] > 0.f) v += red_o[w][i] * exp2f(red_ml[w][h][0] - M);
+        a.part_o[sbase * G * D + i] = v;
     }
     if (tid < G) {
-        a.part_ml[(sbase * G + tid) * 2 + 0] = m_s[tid];
-        a.part_ml[(sbase * G + tid) * 2 + 1] = l_s[tid];
+        a.part_ml[(sbase * G + tid) * 2 + 0] = mrg[tid][0];
+        a.part_ml[(sbase * G + tid) * 2 + 1] = mrg[tid][1];
     }
 }
 
 // Merge the splits of one (unit, head): o = sum_s 2^(m_s - M) o_s / L.
-__global__ __launch_bounds__(128) void decode_combine_kernel(
-    const float *part_ml, const float *part_o, int nsplit, int G, int D,
-    uint16_t *o) {
-    const int uh = blockIdx.x;                  // unit * G + h
-    const int unit = uh / G, h = uh % G;
+// Block (head, unit); thread (slice, channel) sums every SLICES-th split of
+// one channel with its loads unrolled, then the slices are added in LDS.
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(
+    const float *__restrict__ part_ml, const float *__restrict__ part_o,
+    int nsplit, uint16_t *__restrict__ o) {
+    constexpr int SLICES = kThreads / D;
+    __shared__ float w_s[kMaxSplit];
+    __shared__ float red[kThreads];
+    __shared__ float stat[kThreads / 64];
+    const int h = blockIdx.x;
+    const int unit = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const float *ml = part_ml + (size_t)unit * nsplit * G * 2 + h * 2;
+    const float *po = part_o + (size_t)unit * nsplit * G * D + h * D;
+
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s)
-        M = fmaxf(M, part_ml[(((size_t)unit * nsplit + s) * G + h) * 2]);
-    for (int ch = threadIdx.x; ch < D; ch += blockDim.x) {
-        float L = 0.f, acc = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const size_t b = ((size_t)unit * nsplit + s) * G + h;
-            const float w = exp2f(part_ml[b * 2] - M);
-            L += part_ml[b * 2 + 1] * w;
-            acc += part_o[b * D + ch] * w;
-        }
-        o[(size_t)uh * D + ch] = f2h_bits(acc / L);
+    for (int s = tid; s < nsplit; s += kThreads) M = fmaxf(M, ml[(size_t)s * G * 2]);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+    if (lane == 0) stat[wave] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(stat[0], stat[1]), fmaxf(stat[2], stat[3]));
+    float L = 0.f;
+    for (int s = tid; s < nsplit; s += kThreads) {
+        const float l = ml[(size_t)s * G * 2 + 1];
+        const float w = l > 0.f ? exp2f(ml[(size_t)s * G * 2] - M) : 0.f;
+        w_s[s] = w;
+        L += l * w;
+    }
+    for (int off = 32; off > 0; off >>= 1) L += shfl_xor(L, off);
+    __syncthreads();                               // stat reuse, w_s ready
+    if (lane == 0) stat[wave] = L;
+    __syncthreads();
+    L = (stat[0] + stat[1]) + (stat[2] + stat[3]);
+
+    const int ch = tid % D, slice = tid / D;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    int s = slice;
+    for (; s + 3 * SLICES < nsplit; s += 4 * SLICES) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] += po[(size_t)(s + u * SLICES) * G * D + ch] * w_s[s + u * SLICES];
+    }
+    for (; s < nsplit; s += SLICES) v[0] += po[(size_t)s * G * D + ch] * w_s[s];
+    red[tid] = (v[0] + v[1]) + (v[2] + v[3]);
+    __syncthreads();
+    if (slice == 0) {
+        float acc = red[ch];
+        for (int k = 1; k < SLICES; ++k) acc += red[k * D + ch];
+        o[((size_t)unit * G + h) * D + ch] = f2h_bits(acc / L);
     }
 }
 
-int pick_chunk(int units, int n_packed) {
-    for (int ch = kMaxChunk; ch > kMinChunk; ch >>= 1)
-        if ((long)units * ((n_packed + ch - 1) / ch) >= 2048) return ch;
-    return kMinChunk;
+int max_wave_chunk(int g) {
+    return kMaxWaveChunk * g <= 1024 ? kMaxWaveChunk : 1024 / g;
+}
+
+// Largest chunk that still gives ~4 blocks per CU, never more than
+// kMaxSplit - 1 packed splits per unit.
+int pick_chunk(int units, int n_packed, int g) {
+    const int maxw = max_wave_chunk(g);
+    for (int w = maxw; w > kMinWaveChunk; w >>= 1) {
+        const int ch = w * kWaves;
+        const int next = ch / 2;
+        if ((long)units * ((n_packed + ch - 1) / ch) >= 1024) return ch;
+        if ((n_packed + next - 1) / next > kMaxSplit - 1) return ch;
+    }
+    return kMinWaveChunk * kWaves;
+}
+
+template <int D, int G>
+hipError_t launch_decode_dg(const DecArgs &a, int units, hipStream_t stream) {
+    decode_kernel<D, G><<<dim3(a.nsplit, units), kThreads, 0, stream>>>(a);
+    decode_combine_kernel<D, G><<<dim3(G, units), kThreads, 0, stream>>>(
+        a.part_ml, a.part_o, a.nsplit, a.o);
+    return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_decode_d(DecArgs a, int units, int g, hipStream_t stream) {
-    dim3 grid(a.nsplit, units);
+hipError_t launch_decode_d(const DecArgs &a, int units, int g, hipStream_t stream) {
     switch (g) {
-    case 1: decode_kernel<D, 1><<<grid, kThreads, 0, stream>>>(a); break;
-    case 2: decode_kernel<D, 2><<<grid, kThreads, 0, stream>>>(a); break;
-    case 4: decode_kernel<D, 4><<<grid, kThreads, 0, stream>>>(a); break;
-    case 8: decode_kernel<D, 8><<<grid, kThreads, 0, stream>>>(a); break;
+    case 1: return launch_decode_dg<D, 1>(a, units, stream);
+    case 2: return launch_decode_dg<D, 2>(a, units, stream);
+    case 4: return launch_decode_dg<D, 4>(a, units, stream);
+    case 8: return launch_decode_dg<D, 8>(a, units, stream);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+}
+
+size_t part_bytes(int units, int g, int D, int nsplit) {
+    return (size_t)units * nsplit * g * (D + 2) * sizeof(float);
 }
 
 }  // namespace
 
 size_t decode_ws_bytes(int units, int g, int D, int capacity) {
-    const size_t nsplit = (size_t)(capacity + kMinChunk - 1) / kMinChunk + 1;
-    return (size_t)units * nsplit * g * (D + 2) * sizeof(float);
+    const int min_chunk = kMinWaveChunk * kWaves;
+    const int nsplit = std::min((capacity + min_chunk - 1) / min_chunk + 1, kMaxSplit);
+    return part_bytes(units, g, D, nsplit);
+}
+
+int decode_max_capacity(int g) {
+    return (kMaxSplit - 1) * max_wave_chunk(g) * kWaves;
 }
 
 hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
@@ -385,23 +538,20 @@ hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
                          void *ws, size_t ws_bytes, hipStream_t stream) {
     DecArgs a;
     a.q = q;
+    a.o = o;
     a.c = c;
     a.n_packed = n_packed;
     a.n_res = n_res;
-    a.chunk = pick_chunk(units, n_packed);
+    a.chunk = pick_chunk(units, n_packed, g);
     a.n_chunks = (n_packed + a.chunk - 1) / a.chunk;
     a.nsplit = a.n_chunks + (n_res > 0 ? 1 : 0);
     a.qscale = kLog2e / sqrtf((float)c.D);
-    const size_t need = (size_t)units * a.nsplit * g * (c.D + 2) * sizeof(float);
-    if (need > ws_bytes) return hipErrorInvalidValue;
+    if (part_bytes(units, g, c.D, a.nsplit) > ws_bytes || a.nsplit > 512)
+        return hipErrorInvalidValue;
     a.part_ml = static_cast<float *>(ws);
     a.part_o = a.part_ml + (size_t)units * a.nsplit * g * 2;
-    hipError_t e = c.D == 128 ? launch_decode_d<128>(a, units, g, stream)
-                              : launch_decode_d<64>(a, units, g, stream);
-    if (e != hipSuccess) return e;
-    decode_combine_kernel<<<units * g, 128, 0, stream>>>(
-        a.part_ml, a.part_o, a.nsplit, g, c.D, o);
-    return hipGetLastError();
+    return c.D == 128 ? launch_decode_d<128>(a, units, g, stream)
+                      : launch_decode_d<64>(a, units, g, stream);
 }
 
 }  // namespace minikv

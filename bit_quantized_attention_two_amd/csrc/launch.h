@@ -44,8 +44,10 @@ hipError_t launch_append_copy(const uint16_t *k_new, const uint16_t *v_new,
                               int units, int slot, const CacheView &c,
                               hipStream_t stream);
 
-// Decode attention: q, o [units*g][D].
+// Decode attention: q, o [units*g][D].  Caches up to decode_max_capacity(g)
+// packed tokens per unit.
 size_t decode_ws_bytes(int units, int g, int D, int capacity);
+int decode_max_capacity(int g);
 hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
                          int n_packed, int n_res, const CacheView &c,
                          void *ws, size_t ws_bytes, hipStream_t stream);

@@ -41,8 +41,13 @@ __device__ __forceinline__ half8_t load_h8(const uint16_t *p) {
 // S^T accumulator registers directly as the P operand: the contraction slots
 // of k-step (st, a2) are mapped onto the keys those registers hold, and the
 // V^T operand is read from a transposed LDS tile with the same key order.
+//
+// Pipeline: the K/V tile of iteration kt+1 is loaded from HBM into registers
+// while tile kt is multiplied, then written to the other half of a
+// double-buffered LDS tile; one barrier per iteration.  Two waves per SIMD
+// (<= 256 registers) let one wave's MFMAs overlap the other's softmax.
 template <int D>
-__global__ __launch_bounds__(256) void prefill_fwd_kernel(
+__global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o,
     float *__restrict__ lse, int Hq, int Hkv, int n, float sl2) {
@@ -50,8 +55,12 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(
     constexpr int DT = D / 32;
     constexpr int KPAD = D + 8;       // K tile row stride in halves (+16 B)
     constexpr int VPAD = kBN + 4;     // V^T tile row stride in halves (+8 B)
-    __shared__ __attribute__((aligned(16))) uint16_t k_s[kBN * KPAD];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_s[D * VPAD];
+    constexpr int KLD = kBN * D / 8 / 256;        // uint4 K loads per thread
+    constexpr int VTOT = (kBN / 4) * (D / 8);     // 4-key x 8-channel V groups
+    constexpr int VLD = (VTOT + 255) / 256;       // V groups per thread
+    static_assert(KLD >= 1 && KLD * 256 * 8 == kBN * D, "K tile / threads");
+    __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kBN * KPAD];
+    __shared__ __attribute__((aligned(16))) uint16_t vt_s[2][D * VPAD];
 
     const int nqb = (n + kBM - 1) / kBM;
     const int qb = nqb - 1 - (int)blockIdx.x;       // longest rows first
@@ -84,101 +93,136 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(
 
     const int kend = min(n, qb * kBM + kBM);
     const int ntiles = (kend + kBN - 1) / kBN;
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int k0 = kt * kBN;
-        __syncthreads();
-        for (int i = tid; i < kBN * D / 8; i += 256) {
-            const int r = i / (D / 8), cc = i % (D / 8);
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (k0 + r < n)
-                val = *reinterpret_cast<const uint4 *>(kp + (size_t)(k0 + r) * D + cc * 8);
-            *reinterpret_cast<uint4 *>(k_s + r * KPAD + cc * 8) = val;
+
+    uint4 kreg[KLD], vreg[VLD][4];
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < KLD; ++i) {
+            const int idx = tid + 256 * i;
+            const int r = idx / (D / 8), cc = idx % (D / 8);
+            kreg[i] = k0 + r < n ? *reinterpret_cast<const uint4 *>(
+                                       kp + (size_t)(k0 + r) * D + cc * 8)
+                                 : make_uint4(0, 0, 0, 0);
         }
-        for (int i = tid; i < (kBN / 4) * (D / 8); i += 256) {
-            const int kq4 = i / (D / 8), dof = i % (D / 8);
-            uint4 rows[4];
+#pragma unroll
+        for (int i = 0; i < VLD; ++i) {
+            const int idx = tid + 256 * i;
+            const int kq4 = idx / (D / 8), dof = idx % (D / 8);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = k0 + 4 * kq4 + r;
-                rows[r] = key < n ? *reinterpret_cast<const uint4 *>(
-                                        vp + (size_t)key * D + dof * 8)
-                                  : make_uint4(0, 0, 0, 0);
+                vreg[i][r] = (idx < VTOT && key < n)
+                                 ? *reinterpret_cast<const uint4 *>(
+                                       vp + (size_t)key * D + dof * 8)
+                                 : make_uint4(0, 0, 0, 0);
             }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < KLD; ++i) {
+            const int idx = tid + 256 * i;
+            const int r = idx / (D / 8), cc = idx % (D / 8);
+            *reinterpret_cast<uint4 *>(k_s[buf] + r * KPAD + cc * 8) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VLD; ++i) {
+            const int idx = tid + 256 * i;
+            const int kq4 = idx / (D / 8), dof = idx % (D / 8);
+            if (idx >= VTOT) break;
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
                 uint32_t h[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const uint32_t w[4] = {rows[r].x, rows[r].y, rows[r].z, rows[r].w};
+                    const uint32_t w[4] = {vreg[i][r].x, vreg[i][r].y,
+                                           vreg[i][r].z, vreg[i][r].w};
                     h[r] = (w[d >> 1] >> (16 * (d & 1))) & 0xffffu;
                 }
-                *reinterpret_cast<uint2 *>(vt_s + (dof * 8 + d) * VPAD + 4 * kq4) =
+                *reinterpret_cast<uint2 *>(vt_s[buf] + (dof * 8 + d) * VPAD + 4 * kq4) =
                     make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             }
         }
-        __syncthreads();
-        if (k0 > q0 + 31) continue;                 // fully masked for this wave
+    };
 
-        float16_t s[2];
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; ++kt) {
+        const int buf = kt & 1;
+        const int k0 = kt * kBN;
+        const bool more = kt + 1 < ntiles;
+        if (more) load_tile(k0 + kBN);
+
+        if (k0 <= q0 + 31) {                        // not fully masked
+            float16_t s[2];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            s[st] = float16_t{};
+            for (int st = 0; st < 2; ++st) {
+                s[st] = float16_t{};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const half8_t a =
-                    load_h8(k_s + (st * 32 + l32) * KPAD + ks * 16 + 8 * hi);
-                s[st] = mfma32(a, qf[ks], s[st]);
-            }
-        }
-        // s[st][i] = S[key = k0 + 32 st + 8(i/4) + 4 hi + i%4][query = qrow]
-        const bool need_mask = (k0 + kBN - 1 > q0) || (k0 + kBN > n);
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float x = s[st][i] * sl2;
-                if (need_mask) {
-                    const int key = k0 + st * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    if (key > qrow || key >= n) x = -INFINITY;
+                for (int ks = 0; ks < KS; ++ks) {
+                    const half8_t a =
+                        load_h8(k_s[buf] + (st * 32 + l32) * KPAD + ks * 16 + 8 * hi);
+                    s[st] = mfma32(a, qf[ks], s[st]);
                 }
-                s[st][i] = x;
-                tmax = fmaxf(tmax, x);
             }
-        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
-        l_run *= alpha;
+            // s[st][i] = S[key = k0 + 32 st + 8(i/4) + 4 hi + i%4][query = qrow]
+            const bool need_mask = (k0 + kBN - 1 > q0) || (k0 + kBN > n);
+            if (need_mask) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-        m_run = m_new;
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = k0 + st * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+                        if (key > qrow || key >= n) s[st][i] = -INFINITY;
+                    }
+            }
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[st][i]);
+            tmax = fmaxf(tmax, shfl_xor(tmax, 32)) * sl2;
+            const float m_new = fmaxf(m_run, tmax);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            // rescale only when some row max of the wave moved
+            if (__ballot(m_new > m_run) != 0) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            }
+            m_run = m_new;
 
-        half8_t pf[4];                              // k-step (st, a2) = 2 st + a2
-        float l_tile = 0.f;                         // tile sum first: no drift
+            half8_t pf[4];                          // k-step (st, a2) = 2 st + a2
+            float l_tile = 0.f;                     // tile sum first: no drift
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = exp2f(s[st][i] - m_use);
-                l_tile += p;
-                pf[st * 2 + (i >> 3)][i & 7] = (half_t)p;
-            }
-        l_run += l_tile;
+                for (int i = 0; i < 16; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(
+                        __builtin_fmaf(s[st][i], sl2, -m_use));
+                    l_tile += p;
+                    pf[st * 2 + (i >> 3)][i & 7] = (half_t)p;
+                }
+            l_run += l_tile;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+            for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int st = kk >> 1, a2 = kk & 1;
-                const uint16_t *base = vt_s + (dt * 32 + l32) * VPAD + st * 32 +
-                                       16 * a2 + 4 * hi;
-                const half4_t lo4 = *reinterpret_cast<const half4_t *>(base);
-                const half4_t hi4 = *reinterpret_cast<const half4_t *>(base + 8);
-                const half8_t a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3,
-                                                          4, 5, 6, 7);
-                oacc[dt] = mfma32(a, pf[kk], oacc[dt]);
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int st = kk >> 1, a2 = kk & 1;
+                    const uint16_t *base = vt_s[buf] + (dt * 32 + l32) * VPAD + st * 32 +
+                                           16 * a2 + 4 * hi;
+                    const half4_t lo4 = *reinterpret_cast<const half4_t *>(base);
+                    const half4_t hi4 = *reinterpret_cast<const half4_t *>(base + 8);
+                    const half8_t a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3,
+                                                              4, 5, 6, 7);
+                    oacc[dt] = mfma32(a, pf[kk], oacc[dt]);
+                }
             }
         }
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
     }
 
     const float l_tot = l_run + shfl_xor(l_run, 32);
@@ -205,16 +249,19 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(
 // Per wave: 32 key columns, K^T held in registers as the MFMA B operand.
 // S = Q K^T with queries as rows: each lane owns one key column and adds the
 // probabilities of its 16 query rows per 32-row sub-tile; the two lane halves
-// are combined once at the end.
+// are combined once at the end.  The next 64-query tile (and its LSE) is
+// loaded into registers while the current one is used, into a double-buffered
+// LDS tile, with one barrier per tile.
 template <int D>
-__global__ __launch_bounds__(256) void prefill_col_kernel(
+__global__ __launch_bounds__(256, 2) void prefill_col_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const float *__restrict__ lse, float *__restrict__ col, int Hq, int Hkv,
     int n, float sl2) {
     constexpr int KS = D / 16;
     constexpr int QPAD = D + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t q_s[kBQ2 * QPAD];
-    __shared__ float lse_s[kBQ2];
+    constexpr int QLD = kBQ2 * D / 8 / 256;         // uint4 loads per thread
+    __shared__ __attribute__((aligned(16))) uint16_t q_s[2][kBQ2 * QPAD];
+    __shared__ float lse_s[2][kBQ2];
 
     const int kb = blockIdx.x;                      // block 0 has most rows
     const int unit = blockIdx.y;                    // b * Hkv + kvh
@@ -240,23 +287,49 @@ __global__ __launch_bounds__(256) void prefill_col_kernel(
     // probabilities added to a large column total do not drift low.
     float colacc = 0.f, colcomp = 0.f;
 
-    for (int h = 0; h < g; ++h) {
+    // flattened (head, query tile) sequence
+    const int qstart = kb * kBK2;
+    const int tiles_per_head = (n - qstart + kBQ2 - 1) / kBQ2;
+    const int ntiles = g * tiles_per_head;
+    uint4 qreg[QLD];
+    float lreg = 0.f;
+    auto load_tile = [&](int t) {
+        const int h = t / tiles_per_head;
+        const int qt0 = qstart + (t % tiles_per_head) * kBQ2;
         const size_t bhq = (size_t)b * Hq + kvh * g + h;
         const uint16_t *qp = q + bhq * n * D;
-        const float *lp = lse + bhq * n;
-        for (int qt0 = kb * kBK2; qt0 < n; qt0 += kBQ2) {
-            __syncthreads();
-            for (int i = tid; i < kBQ2 * D / 8; i += 256) {
-                const int r = i / (D / 8), cc = i % (D / 8);
-                uint4 val = make_uint4(0, 0, 0, 0);
-                if (qt0 + r < n)
-                    val = *reinterpret_cast<const uint4 *>(qp + (size_t)(qt0 + r) * D + cc * 8);
-                *reinterpret_cast<uint4 *>(q_s + r * QPAD + cc * 8) = val;
-            }
-            if (tid < kBQ2)
-                lse_s[tid] = (qt0 + tid < n) ? lp[qt0 + tid] * kLog2e : INFINITY;
-            __syncthreads();
-            if (qt0 + kBQ2 - 1 < k0w) continue;     // every query precedes every key
+#pragma unroll
+        for (int i = 0; i < QLD; ++i) {
+            const int idx = tid + 256 * i;
+            const int r = idx / (D / 8), cc = idx % (D / 8);
+            qreg[i] = qt0 + r < n ? *reinterpret_cast<const uint4 *>(
+                                        qp + (size_t)(qt0 + r) * D + cc * 8)
+                                  : make_uint4(0, 0, 0, 0);
+        }
+        if (tid < kBQ2)
+            lreg = (qt0 + tid < n) ? lse[bhq * n + qt0 + tid] * kLog2e : INFINITY;
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < QLD; ++i) {
+            const int idx = tid + 256 * i;
+            const int r = idx / (D / 8), cc = idx % (D / 8);
+            *reinterpret_cast<uint4 *>(q_s[buf] + r * QPAD + cc * 8) = qreg[i];
+        }
+        if (tid < kBQ2) lse_s[buf][tid] = lreg;
+    };
+
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        const int qt0 = qstart + (t % tiles_per_head) * kBQ2;
+        const bool more = t + 1 < ntiles;
+        if (more) load_tile(t + 1);
+        if (qt0 + kBQ2 - 1 >= k0w) {               // some query sees some key
             float tile = 0.f;
 #pragma unroll
             for (int qs = 0; qs < 2; ++qs) {
@@ -264,7 +337,7 @@ __global__ __launch_bounds__(256) void prefill_col_kernel(
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const half8_t a =
-                        load_h8(q_s + (qs * 32 + l32) * QPAD + ks * 16 + 8 * hi);
+                        load_h8(q_s[buf] + (qs * 32 + l32) * QPAD + ks * 16 + 8 * hi);
                     s = mfma32(a, kf[ks], s);
                 }
                 // s[i] = S[query = qt0 + 32 qs + 8(i/4) + 4 hi + i%4][key]
@@ -273,16 +346,19 @@ __global__ __launch_bounds__(256) void prefill_col_kernel(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int r = qs * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    float p = exp2f(s[i] * sl2 - lse_s[r]);
+                    float p = __builtin_amdgcn_exp2f(
+                        __builtin_fmaf(s[i], sl2, -lse_s[buf][r]));
                     if (need_mask && (qt0 + r < key || qt0 + r >= n)) p = 0.f;
                     tile += p;
                 }
             }
             const float y = tile - colcomp;
-            const float t = colacc + y;
-            colcomp = (t - colacc) - y;
-            colacc = t;
+            const float tt = colacc + y;
+            colcomp = (tt - colacc) - y;
+            colacc = tt;
         }
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
     }
     colacc += shfl_xor(colacc, 32);
     if (hi == 0 && key < n) col[(size_t)unit * n + key] = colacc;

@@ -301,7 +301,9 @@ def decode_attn(dims, cache, q, o=None, ws=None, stream=None):
     _need(q, torch.float16, shape, "q")
     o = torch.empty_like(q) if o is None else o
     if ws is None:
-        ws = torch.empty(decode_ws_bytes(dims, cache.capacity),
+        # zero-filled once: its first bytes are the per-unit completion
+        # counters, which every call leaves at zero again
+        ws = torch.zeros(decode_ws_bytes(dims, cache.capacity),
                          dtype=torch.uint8, device=q.device)
     _check(lib().minikv_decode_attn(ctypes.byref(dims), ctypes.byref(cache.c),
                                     _ptr(q), _ptr(o), _ptr(ws),

@@ -223,8 +223,13 @@ MINIKV_API int32_t minikv_append(const minikv_dims *dims, minikv_layer_cache *ca
  *   q fp16 [B][Hq][D];  o fp16 [B][Hq][D]
  *   o[b][hq] = softmax_t(q . k_t / sqrt(D)) v_t over the n_packed packed
  *   tokens (dequantised) and the n_res residual tokens of unit
- *   (b, hq / g).  ws: minikv_decode_ws_bytes(dims, capacity) bytes.
- * EINVAL if the cache holds no token. */
+ *   (b, hq / g).
+ * ws: at least minikv_decode_ws_bytes(dims, capacity) bytes of scratch for
+ *   the split partial results; calls that share a workspace must not overlap
+ *   in time.
+ * EINVAL if the cache holds no token; EUNSUPPORTED if capacity exceeds
+ * 511 * 2048 packed tokens (g <= 2; 511 * 1024 for g = 4, 511 * 512 for
+ * g = 8). */
 MINIKV_API int32_t minikv_decode_attn(const minikv_dims *dims,
                            const minikv_layer_cache *cache, const void *q,
                            void *o, void *ws, size_t ws_bytes, void *stream);
