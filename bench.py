@@ -6,8 +6,9 @@ layer as a model runs it:
   prefill: for every layer, minikv_prefill_select (pass 1: attention output
            + LSE; pass 2: per-key cumulative scores; top-k + recent window)
            and minikv_pack (INT2 keys/values, fp16 residual tail);
-  decode:  for every decode step and every layer, minikv_append (with the
-           residual flush every 128 tokens) and minikv_decode_attn.
+  decode:  for every decode step and every layer, minikv_append_decode
+           (append the new token -- flushing the residual every 128 tokens --
+           and attend over the packed cache plus the residual).
 Inputs (prompt Q/K/V of every layer and the decode-step q/k/v) are resident
 in HBM before the timed region.
 
@@ -150,11 +151,12 @@ def main():
         for s in range(S):
             for l in range(L):
                 cache = caches[l]
-                minikv.append(dims, cache, dk[s % ns, l % nl], dv[s % ns, l % nl])
+                # append + decode attention, fused unless the residual flushes
+                minikv.append_decode(dims, cache, dk[s % ns, l % nl],
+                                     dv[s % ns, l % nl], dq[s % ns, l % nl],
+                                     o=od, ws=ws_dec)
                 dec_bytes_per_call.append(decode_bytes(c, cache.n_packed,
                                                        cache.n_res))
-                minikv.decode_attn(dims, cache, dq[s % ns, l % nl], o=od,
-                                   ws=ws_dec)
 
     def capture(fn, side):
         g = torch.cuda.CUDAGraph()

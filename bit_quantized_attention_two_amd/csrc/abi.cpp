@@ -416,15 +416,12 @@ int32_t minikv_append(const minikv_dims *d, minikv_layer_cache *c,
     return ok();
 }
 
-int32_t minikv_decode_attn(const minikv_dims *d, const minikv_layer_cache *c,
-                           const void *q, void *o, void *ws, size_t ws_bytes,
-                           void *stream) {
-    CHECK(check_dims(d));
-    CHECK(check_cache(d, c));
+static int32_t check_decode(const minikv_dims *d, const minikv_layer_cache *c,
+                            const void *q, const void *o, const void *ws,
+                            size_t ws_bytes) {
     CHECK_PTR(q, "q");
     CHECK_PTR(o, "o");
     CHECK_PTR(ws, "ws");
-    if (c->n_packed + c->n_res == 0) return fail(MINIKV_EINVAL, "cache holds no token");
     const int units = d->batch * d->n_kv_heads;
     const int g = d->n_q_heads / d->n_kv_heads;
     if (c->capacity > minikv::decode_max_capacity(g))
@@ -433,12 +430,53 @@ int32_t minikv_decode_attn(const minikv_dims *d, const minikv_layer_cache *c,
     const size_t need = minikv::decode_ws_bytes(units, g, d->head_dim, c->capacity);
     if (ws_bytes < need)
         return fail(MINIKV_EINVAL, "workspace too small: %zu < %zu", ws_bytes, need);
+    return MINIKV_OK;
+}
+
+int32_t minikv_decode_attn(const minikv_dims *d, const minikv_layer_cache *c,
+                           const void *q, void *o, void *ws, size_t ws_bytes,
+                           void *stream) {
+    CHECK(check_dims(d));
+    CHECK(check_cache(d, c));
+    CHECK(check_decode(d, c, q, o, ws, ws_bytes));
+    if (c->n_packed + c->n_res == 0) return fail(MINIKV_EINVAL, "cache holds no token");
     CHECK(check_device());
+    const int units = d->batch * d->n_kv_heads;
+    const int g = d->n_q_heads / d->n_kv_heads;
     return hip_status(minikv::launch_decode(static_cast<const uint16_t *>(q),
                                             static_cast<uint16_t *>(o), units, g,
-                                            c->n_packed, c->n_res, view_of(d, c), ws,
-                                            ws_bytes, static_cast<hipStream_t>(stream)),
+                                            c->n_packed, c->n_res, view_of(d, c),
+                                            nullptr, nullptr, ws, ws_bytes,
+                                            static_cast<hipStream_t>(stream)),
                       "decode launch");
+}
+
+int32_t minikv_append_decode(const minikv_dims *d, minikv_layer_cache *c,
+                             const void *k_new, const void *v_new, const void *q,
+                             void *o, void *ws, size_t ws_bytes, void *stream) {
+    CHECK(check_dims(d));
+    CHECK(check_cache(d, c));
+    CHECK_PTR(k_new, "k_new");
+    CHECK_PTR(v_new, "v_new");
+    CHECK(check_decode(d, c, q, o, ws, ws_bytes));
+    const bool flush = c->n_res + 1 == d->residual_cap;
+    if (flush) {
+        // the residual is packed first: the separate calls, in order
+        CHECK(minikv_append(d, c, k_new, v_new, stream));
+        return minikv_decode_attn(d, c, q, o, ws, ws_bytes, stream);
+    }
+    CHECK(check_device());
+    const int units = d->batch * d->n_kv_heads;
+    const int g = d->n_q_heads / d->n_kv_heads;
+    const int32_t st = hip_status(
+        minikv::launch_decode(static_cast<const uint16_t *>(q), static_cast<uint16_t *>(o),
+                              units, g, c->n_packed, c->n_res + 1, view_of(d, c),
+                              static_cast<const uint16_t *>(k_new),
+                              static_cast<const uint16_t *>(v_new), ws, ws_bytes,
+                              static_cast<hipStream_t>(stream)),
+        "append+decode launch");
+    if (st == MINIKV_OK) c->n_res += 1;
+    return st;
 }
 
 }  // extern "C"

@@ -25,9 +25,14 @@
 // finish would need device-scope fences, which on this multi-die part write
 // back and invalidate the L2 of every block that takes them.)
 //
-// Global loads are issued ahead of their use -- the next 16-token key row
-// while the current one is reduced, four value rows at a time -- so that
-// each wave keeps several HBM round trips in flight.
+// Latency: every global load is issued ahead of its use and never predicated
+// off (indices are clamped; extra rows get weight 0).  The first batch of
+// value rows is requested at kernel start together with the key rows, the
+// next key row and value batch while the current ones are used.
+//
+// Fused append: when the caller passes a new token, the residual block reads
+// it from the call's input, uses it as residual slot `new_slot`, and stores
+// it there for later calls.
 #include <algorithm>
 
 #include "common.h"
@@ -40,7 +45,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kMinWaveChunk = 64;
 constexpr int kMaxWaveChunk = 512;
-constexpr int kMaxSplit = 512;            // LDS rows of the combine kernel
+constexpr int kMaxSplit = 512;
 
 struct DecArgs {
     const uint16_t *q;
@@ -48,8 +53,10 @@ struct DecArgs {
     CacheView c;
     int n_packed, n_res, chunk, n_chunks, nsplit;
     float qscale;
-    float *part_ml;     // [units][nsplit][G][2]
-    float *part_o;      // [units][nsplit][G][D]
+    const uint16_t *k_new, *v_new;   // nullable: fused append of one token
+    int new_slot;                    // residual slot of the new token
+    float *part_ml;                  // [units][nsplit][G][2]
+    float *part_o;                   // [units][nsplit][G][D]
 };
 
 template <int CTRL>
@@ -107,6 +114,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     constexpr int WPT = D / 16;               // value words per token
     constexpr int TS = 64 / WPT;              // tokens per V pass of a wave
     constexpr int MAXW = kMaxWaveChunk * G <= 1024 ? kMaxWaveChunk : 1024 / G;
+    constexpr int VB = G <= 2 ? 8 : 4;        // value rows per load batch
     const int unit = blockIdx.y;
     const int split = blockIdx.x;
     const int tid = threadIdx.x;
@@ -133,6 +141,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     const uint16_t *qu = a.q + (size_t)unit * G * D;
     float *ps = p_s[wave];
 
+    // value-row batch of this lane: requested now, used after the softmax
+    const int vj = lane % WPT;                // channels 16 vj .. 16 vj + 15
+    const int vts = lane / WPT;
+    const int gpt = D / c.Gv;
+    const int gsel = (vj * 16) / c.Gv;
+    const uint32_t *vw = reinterpret_cast<const uint32_t *>(c.vq) +
+                         (size_t)unit * c.vq_unit() + (size_t)t0 * WPT + vj;
+    const uint16_t *vsr = c.vs + (size_t)unit * c.vm_unit() + (size_t)t0 * gpt + gsel;
+    const uint16_t *vzr = c.vz + (size_t)unit * c.vm_unit() + (size_t)t0 * gpt + gsel;
+    uint32_t vwd[VB];
+    uint16_t vsb[VB], vzb[VB];
+    auto load_vbatch = [&](int tb) {
+#pragma unroll
+        for (int i = 0; i < VB; ++i) {
+            const int t = min(tb + i * TS, nt - 1);
+            vwd[i] = vw[(size_t)t * WPT];
+            vsb[i] = vsr[(size_t)t * gpt];
+            vzb[i] = vzr[(size_t)t * gpt];
+        }
+    };
+    if (!resid && nt > 0) load_vbatch(vts);
+
     // --------------------------------------------------------- logits
     float m_w[G];
 #pragma unroll
@@ -154,8 +184,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         const uint16_t *ks = c.ks + (size_t)unit * c.km_unit();
         const uint16_t *kz = c.kz + (size_t)unit * c.km_unit();
         const int nrows = nt >> 4;
-        // row r0 + rsub of each 4-row pass; the next pass's data is loaded
-        // before the current one is used
         uint32_t wds[CPL];
         float sv[CPL], zv[CPL];
         auto load_row = [&](int row, uint32_t *w, float *sp, float *zp) {
@@ -165,9 +193,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             load_halves<CPL>(ks + (size_t)grp * D + CPL * part, sp);
             load_halves<CPL>(kz + (size_t)grp * D + CPL * part, zp);
         };
-        // loads are never predicated off: a row past the end re-reads the
-        // last row and its result is discarded, so the loads of the next
-        // pass are in flight while this one computes
+        // row r0 + rsub of each 4-row pass; a row past the end re-reads the
+        // last row and its result is discarded
         if (nrows > 0) load_row(min(rsub, nrows - 1), wds, sv, zv);
         for (int r0 = 0; r0 < nrows; r0 += 4) {
             const int row = r0 + rsub;
@@ -233,12 +260,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
             }
         }
     } else {
+        // residual: one lane per token, fp16 keys; the fused new token is
+        // read from the call's input
         const uint16_t *kr = c.kres + (size_t)unit * c.res_unit();
         for (int t = lane; t < nt; t += 64) {
+            const int slot = t0 + t;
+            const uint16_t *krow = (a.k_new && slot == a.new_slot)
+                                       ? a.k_new + (size_t)unit * D
+                                       : kr + (size_t)slot * D;
             float acc[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) acc[h] = 0.f;
-            const uint4 *row = reinterpret_cast<const uint4 *>(kr + (size_t)(t0 + t) * D);
+            const uint4 *row = reinterpret_cast<const uint4 *>(krow);
 #pragma unroll 2
             for (int i = 0; i < D / 8; ++i) {
                 float kf[8];
@@ -258,6 +291,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                 m_w[h] = fmaxf(m_w[h], v);
             }
         }
+        // store the new token into its residual slot for later calls
+        if (a.k_new && wave == 0 && lane < 2 * (D / 8)) {
+            const int part = lane % (D / 8);
+            const bool isv = lane >= D / 8;
+            const uint16_t *src = (isv ? a.v_new : a.k_new) + (size_t)unit * D;
+            uint16_t *dst = (isv ? c.vres : c.kres) + (size_t)unit * c.res_unit() +
+                            (size_t)a.new_slot * D;
+            reinterpret_cast<uint4 *>(dst)[part] = reinterpret_cast<const uint4 *>(src)[part];
+        }
     }
 
     // ------------------------------------------------ wave softmax stats
@@ -271,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     for (int t = lane; t < nt; t += 64)
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float p = exp2f(ps[t * G + h] - m_w[h]);
+            const float p = __builtin_amdgcn_exp2f(ps[t * G + h] - m_w[h]);
             ps[t * G + h] = p;
             l_w[h] += p;
         }
@@ -282,14 +324,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 
     // ----------------------------------------------------------- P . V
     if (!resid) {
-        const int j = lane % WPT;             // channels 16 j .. 16 j + 15
-        const int ts = lane / WPT;
-        const int gpt = D / c.Gv;
-        const int gsel = (j * 16) / c.Gv;
-        const uint32_t *vw = reinterpret_cast<const uint32_t *>(c.vq) +
-                             (size_t)unit * c.vq_unit() + (size_t)t0 * WPT + j;
-        const uint16_t *vsr = c.vs + (size_t)unit * c.vm_unit() + (size_t)t0 * gpt + gsel;
-        const uint16_t *vzr = c.vz + (size_t)unit * c.vm_unit() + (size_t)t0 * gpt + gsel;
         float acc[G][16];
         float zs[G];
 #pragma unroll
@@ -298,27 +332,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
         }
-        constexpr int VB = 4;                 // value rows loaded per batch
-        for (int tb = ts; tb < nt; tb += VB * TS) {
-            // unpredicated loads (indices clamped to the last token; the
-            // extra rows get p = 0), all issued before the first use
-            uint32_t wdb[VB];
-            uint16_t sb[VB], zb[VB];
+        for (int tb = vts; tb < nt; tb += VB * TS) {
+            uint32_t cwd[VB];
+            uint16_t csb[VB], czb[VB];
 #pragma unroll
             for (int i = 0; i < VB; ++i) {
-                const int t = min(tb + i * TS, nt - 1);
-                wdb[i] = vw[(size_t)t * WPT];
-                sb[i] = vsr[(size_t)t * gpt];
-                zb[i] = vzr[(size_t)t * gpt];
+                cwd[i] = vwd[i];
+                csb[i] = vsb[i];
+                czb[i] = vzb[i];
             }
+            load_vbatch(tb + VB * TS);            // next batch (clamped)
 #pragma unroll
             for (int i = 0; i < VB; ++i) {
                 const int t = tb + i * TS;
                 const bool ok = t < nt;
                 const int tc = min(t, nt - 1);
-                const float s = h2f(sb[i]);
-                const float z = h2f(zb[i]);
-                const uint32_t wd = wdb[i];
+                const float s = h2f(csb[i]);
+                const float z = h2f(czb[i]);
                 float pss[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
@@ -329,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     // bytes of m: codes of channels k, 4+k, 8+k, 12+k
-                    const uint32_t m = (wd >> (2 * k)) & 0x03030303u;
+                    const uint32_t m = (cwd[i] >> (2 * k)) & 0x03030303u;
                     const float c0 = (float)(m & 0xff);
                     const float c1 = (float)((m >> 8) & 0xff);
                     const float c2 = (float)((m >> 16) & 0xff);
@@ -356,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) red_o[wave][h * D + j * 16 + e] = acc[h][e];
+                for (int e = 0; e < 16; ++e) red_o[wave][h * D + vj * 16 + e] = acc[h][e];
     } else {
         constexpr int CPT = D / 8;            // uint4 per residual row
         constexpr int RTS = 64 / CPT;
@@ -369,8 +399,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
         for (int t = ts; t < nt; t += RTS) {
+            const int slot = t0 + t;
+            const uint16_t *vrow = (a.v_new && slot == a.new_slot)
+                                       ? a.v_new + (size_t)unit * D
+                                       : vr + (size_t)slot * D;
             float vf[8];
-            unpack8h(reinterpret_cast<const uint4 *>(vr + (size_t)(t0 + t) * D)[c8], vf);
+            unpack8h(reinterpret_cast<const uint4 *>(vrow)[c8], vf);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 const float p = ps[t * G + h];
@@ -406,7 +440,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][tid][0]);
         float L = 0.f;
         for (int w = 0; w < kWaves; ++w)
-            if (red_ml[w][tid][1] > 0.f) L += red_ml[w][tid][1] * exp2f(red_ml[w][tid][0] - M);
+            if (red_ml[w][tid][1] > 0.f)
+                L += red_ml[w][tid][1] * __builtin_amdgcn_exp2f(red_ml[w][tid][0] - M);
         mrg[tid][0] = M;
         mrg[tid][1] = L;
     }
@@ -417,7 +452,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         const float M = mrg[h][0];
         float v = 0.f;
         for (int w = 0; w < kWaves; ++w)
-            if (red_ml[w][h][1] > 0.f) v += red_o[w][i] * exp2f(red_ml[w][h][0] - M);
+            if (red_ml[w][h][1] > 0.f)
+                v += red_o[w][i] * __builtin_amdgcn_exp2f(red_ml[w][h][0] - M);
         a.part_o[sbase * G * D + i] = v;
     }
     if (tid < G) {
@@ -427,56 +463,68 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
 }
 
 // Merge the splits of one (unit, head): o = sum_s 2^(m_s - M) o_s / L.
-// Block (head, unit); thread (slice, channel) sums every SLICES-th split of
-// one channel with its loads unrolled, then the slices are added in LDS.
+// Block (head, unit); thread (slice, channel) takes every SLICES-th split of
+// one channel.  It loads a batch of up to NB splits' (max, sum, o) at once
+// and folds it into a running (max, sum, o); the slices are then merged in
+// LDS.  A workload with at most SLICES * NB splits per unit needs a single
+// round trip to memory.
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     const float *__restrict__ part_ml, const float *__restrict__ part_o,
     int nsplit, uint16_t *__restrict__ o) {
     constexpr int SLICES = kThreads / D;
-    __shared__ float w_s[kMaxSplit];
-    __shared__ float red[kThreads];
-    __shared__ float stat[kThreads / 64];
+    constexpr int NB = 8;
+    __shared__ float r_m[kThreads], r_l[kThreads], r_o[kThreads];
     const int h = blockIdx.x;
     const int unit = blockIdx.y;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const float *ml = part_ml + (size_t)unit * nsplit * G * 2 + h * 2;
-    const float *po = part_o + (size_t)unit * nsplit * G * D + h * D;
-
-    float M = -INFINITY;
-    for (int s = tid; s < nsplit; s += kThreads) M = fmaxf(M, ml[(size_t)s * G * 2]);
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
-    if (lane == 0) stat[wave] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(stat[0], stat[1]), fmaxf(stat[2], stat[3]));
-    float L = 0.f;
-    for (int s = tid; s < nsplit; s += kThreads) {
-        const float l = ml[(size_t)s * G * 2 + 1];
-        const float w = l > 0.f ? exp2f(ml[(size_t)s * G * 2] - M) : 0.f;
-        w_s[s] = w;
-        L += l * w;
-    }
-    for (int off = 32; off > 0; off >>= 1) L += shfl_xor(L, off);
-    __syncthreads();                               // stat reuse, w_s ready
-    if (lane == 0) stat[wave] = L;
-    __syncthreads();
-    L = (stat[0] + stat[1]) + (stat[2] + stat[3]);
-
     const int ch = tid % D, slice = tid / D;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    int s = slice;
-    for (; s + 3 * SLICES < nsplit; s += 4 * SLICES) {
+    const float *ml = part_ml + (size_t)unit * nsplit * G * 2 + h * 2;
+    const float *po = part_o + (size_t)unit * nsplit * G * D + h * D + ch;
+
+    float m_run = -INFINITY, l_run = 0.f, o_run = 0.f;
+    for (int s0 = slice; s0 < nsplit; s0 += NB * SLICES) {
+        float mb[NB], lb[NB], ob[NB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            v[u] += po[(size_t)(s + u * SLICES) * G * D + ch] * w_s[s + u * SLICES];
+        for (int i = 0; i < NB; ++i) {
+            const int s = min(s0 + i * SLICES, nsplit - 1);
+            mb[i] = ml[(size_t)s * G * 2];
+            lb[i] = ml[(size_t)s * G * 2 + 1];
+            ob[i] = po[(size_t)s * G * D];
+        }
+        float mx = m_run;
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            if (s0 + i * SLICES < nsplit && lb[i] > 0.f) mx = fmaxf(mx, mb[i]);
+        if (mx == -INFINITY) continue;
+        const float sc = __builtin_amdgcn_exp2f(m_run - mx);
+        l_run *= sc;
+        o_run *= sc;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (s0 + i * SLICES < nsplit && lb[i] > 0.f) {
+                const float w = __builtin_amdgcn_exp2f(mb[i] - mx);
+                l_run += lb[i] * w;
+                o_run += ob[i] * w;
+            }
+        }
+        m_run = mx;
     }
-    for (; s < nsplit; s += SLICES) v[0] += po[(size_t)s * G * D + ch] * w_s[s];
-    red[tid] = (v[0] + v[1]) + (v[2] + v[3]);
+    r_m[tid] = m_run;
+    r_l[tid] = l_run;
+    r_o[tid] = o_run;
     __syncthreads();
     if (slice == 0) {
-        float acc = red[ch];
-        for (int k = 1; k < SLICES; ++k) acc += red[k * D + ch];
+        float M = -INFINITY;
+        for (int k = 0; k < SLICES; ++k) M = fmaxf(M, r_m[k * D + ch]);
+        float L = 0.f, acc = 0.f;
+        for (int k = 0; k < SLICES; ++k) {
+            if (r_l[k * D + ch] > 0.f) {
+                const float w = __builtin_amdgcn_exp2f(r_m[k * D + ch] - M);
+                L += r_l[k * D + ch] * w;
+                acc += r_o[k * D + ch] * w;
+            }
+        }
         o[((size_t)unit * G + h) * D + ch] = f2h_bits(acc / L);
     }
 }
@@ -535,6 +583,7 @@ int decode_max_capacity(int g) {
 
 hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
                          int n_packed, int n_res, const CacheView &c,
+                         const uint16_t *k_new, const uint16_t *v_new,
                          void *ws, size_t ws_bytes, hipStream_t stream) {
     DecArgs a;
     a.q = q;
@@ -546,7 +595,10 @@ hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
     a.n_chunks = (n_packed + a.chunk - 1) / a.chunk;
     a.nsplit = a.n_chunks + (n_res > 0 ? 1 : 0);
     a.qscale = kLog2e / sqrtf((float)c.D);
-    if (part_bytes(units, g, c.D, a.nsplit) > ws_bytes || a.nsplit > 512)
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.new_slot = n_res - 1;
+    if (part_bytes(units, g, c.D, a.nsplit) > ws_bytes || a.nsplit > kMaxSplit)
         return hipErrorInvalidValue;
     a.part_ml = static_cast<float *>(ws);
     a.part_o = a.part_ml + (size_t)units * a.nsplit * g * 2;

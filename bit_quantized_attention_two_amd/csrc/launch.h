@@ -48,8 +48,11 @@ hipError_t launch_append_copy(const uint16_t *k_new, const uint16_t *v_new,
 // packed tokens per unit.
 size_t decode_ws_bytes(int units, int g, int D, int capacity);
 int decode_max_capacity(int g);
+// k_new/v_new [units][D] (nullable): a token appended in the same launch; it
+// is residual slot n_res - 1 and is stored there by the kernel.
 hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
                          int n_packed, int n_res, const CacheView &c,
+                         const uint16_t *k_new, const uint16_t *v_new,
                          void *ws, size_t ws_bytes, hipStream_t stream);
 
 // Prefill, both passes.

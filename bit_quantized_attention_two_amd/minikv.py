@@ -79,6 +79,8 @@ def lib():
             "minikv_pack": ([D, _i32, _P, _P, _P, _i32, C, _P], _i32),
             "minikv_append": ([D, C, _P, _P, _P], _i32),
             "minikv_decode_attn": ([D, C, _P, _P, _P, _sz, _P], _i32),
+            "minikv_append_decode": ([D, C, _P, _P, _P, _P, _P, _sz, _P],
+                                     _i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -93,7 +95,7 @@ EXPORTED = ("minikv_version", "minikv_status_str", "minikv_last_error",
             "minikv_cache_layout", "minikv_prefill_ws_bytes",
             "minikv_decode_ws_bytes", "minikv_prefill_attn", "minikv_select",
             "minikv_prefill_select", "minikv_pack", "minikv_append",
-            "minikv_decode_attn")
+            "minikv_decode_attn", "minikv_append_decode")
 
 
 def status_str(s):
@@ -301,12 +303,27 @@ def decode_attn(dims, cache, q, o=None, ws=None, stream=None):
     _need(q, torch.float16, shape, "q")
     o = torch.empty_like(q) if o is None else o
     if ws is None:
-        # zero-filled once: its first bytes are the per-unit completion
-        # counters, which every call leaves at zero again
-        ws = torch.zeros(decode_ws_bytes(dims, cache.capacity),
+        ws = torch.empty(decode_ws_bytes(dims, cache.capacity),
                          dtype=torch.uint8, device=q.device)
     _check(lib().minikv_decode_attn(ctypes.byref(dims), ctypes.byref(cache.c),
                                     _ptr(q), _ptr(o), _ptr(ws),
                                     ws.numel() * ws.element_size(),
                                     _stream(stream)))
+    return o
+
+
+def append_decode(dims, cache, k_new, v_new, q, o=None, ws=None, stream=None):
+    """append(k_new, v_new) then decode_attn(q), fused when no flush is due."""
+    kshape = (dims.batch, dims.n_kv_heads, dims.head_dim)
+    _need(k_new, torch.float16, kshape, "k_new")
+    _need(v_new, torch.float16, kshape, "v_new")
+    _need(q, torch.float16, (dims.batch, dims.n_q_heads, dims.head_dim), "q")
+    o = torch.empty_like(q) if o is None else o
+    if ws is None:
+        ws = torch.empty(decode_ws_bytes(dims, cache.capacity),
+                         dtype=torch.uint8, device=q.device)
+    _check(lib().minikv_append_decode(
+        ctypes.byref(dims), ctypes.byref(cache.c), _ptr(k_new), _ptr(v_new),
+        _ptr(q), _ptr(o), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
     return o

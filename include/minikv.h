@@ -234,6 +234,18 @@ MINIKV_API int32_t minikv_decode_attn(const minikv_dims *dims,
                            const minikv_layer_cache *cache, const void *q,
                            void *o, void *ws, size_t ws_bytes, void *stream);
 
+/* minikv_append followed by minikv_decode_attn (the new token attends to
+ * itself), with the same results bit for bit.  On a step that does not flush
+ * the residual, the append happens inside the decode launch: the kernel reads
+ * the new token from k_new/v_new and stores it in its residual slot.  On a
+ * flushing step it runs the two calls in order.  Arguments and errors as for
+ * the two calls; nothing changes if either would fail. */
+MINIKV_API int32_t minikv_append_decode(const minikv_dims *dims,
+                                        minikv_layer_cache *cache,
+                                        const void *k_new, const void *v_new,
+                                        const void *q, void *o, void *ws,
+                                        size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -132,3 +132,30 @@ def test_decode_full_size(cfg_id):
             assert np.array_equal(gc[gname][u], getattr(oc, oname)[b, h]), \
                 (gname, b, h)
     _decode_and_compare(torch, mk, dims, cache, oc, q, units)
+
+
+@pytest.mark.parametrize("g,D", [(1, 128), (4, 128), (2, 64)])
+def test_append_decode_equals_separate_calls(g, D):
+    """The fused entry point gives the same bits as minikv_append followed by
+    minikv_decode_attn, across a residual flush, and leaves the same cache."""
+    torch, mk = require_gpu()
+    from gpu_util import cache_to_numpy
+    B, Hkv, n, m = 2, 2, 700, 333
+    dims, ca, _ = _build(torch, mk, B, Hkv, g, D, 16, 16, n, m, seed=21,
+                         check_bits=False)
+    _, cb, _ = _build(torch, mk, B, Hkv, g, D, 16, 16, n, m, seed=21,
+                      check_bits=False)
+    say("append_decode", dict(g=g, D=D))
+    for s in range(140):
+        q, kn, vn = synth.gen_decode_step(21, 0, s, B, Hkv * g, Hkv, D)
+        q, kn, vn = dev16(torch, q), dev16(torch, kn), dev16(torch, vn)
+        mk.append(dims, ca, kn, vn)
+        oa = mk.decode_attn(dims, ca, q)
+        ob = mk.append_decode(dims, cb, kn, vn, q)
+        assert (ca.n_packed, ca.n_res) == (cb.n_packed, cb.n_res)
+        if s % 23 == 0 or ca.n_res in (0, 1):
+            torch.cuda.synchronize()
+            assert torch.equal(oa, ob), s
+            xa, xb = cache_to_numpy(ca), cache_to_numpy(cb)
+            for name in xa:
+                assert np.array_equal(xa[name], xb[name]), (s, name)
