@@ -33,6 +33,25 @@ __device__ __forceinline__ half8_t load_h8(const uint16_t *p) {
     return *reinterpret_cast<const half8_t *>(p);
 }
 
+typedef short short4_lds __attribute__((ext_vector_type(4)));
+// Native 16-byte vector; HIP's uint4 struct in a small array is not promoted
+// to registers when filled from global memory.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// gfx950 transposing LDS read.  Within each group of 16 lanes, lane i gets
+// element i % 4 of the 8-byte rows addressed by lanes i/4, i/4+4, i/4+8 and
+// i/4+12 of its group (checked on the device).  With lane L addressing key
+// row (kb + L/4) at channel (d0 + 4 (L%4)) of a row-major [key][d] tile,
+// lane L receives channel d0 + L of keys kb .. kb+3: the K-contiguous
+// operand layout the MFMA wants, without a transposed copy of the tile.
+__device__ __forceinline__ half4_t ds_read_tr16(const uint16_t *lds) {
+    const short4_lds v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4_lds *)(lds));
+    return __builtin_bit_cast(half4_t, v);
+}
+
+template <bool B> struct bool_c { static constexpr bool value = B; };
+
 // ---------------------------------------------------------------- pass 1
 //
 // Per wave: 32 query rows.  S^T = K Q^T (keys as MFMA rows, queries as
@@ -40,12 +59,15 @@ __device__ __forceinline__ half8_t load_h8(const uint16_t *p) {
 // single exchange between the two lane halves.  O^T = V^T P^T re-uses the
 // S^T accumulator registers directly as the P operand: the contraction slots
 // of k-step (st, a2) are mapped onto the keys those registers hold, and the
-// V^T operand is read from a transposed LDS tile with the same key order.
+// matching V^T operand is read from the row-major V tile with the
+// transposing LDS read.
 //
 // Pipeline: the K/V tile of iteration kt+1 is loaded from HBM into registers
 // while tile kt is multiplied, then written to the other half of a
-// double-buffered LDS tile; one barrier per iteration.  Two waves per SIMD
-// (<= 256 registers) let one wave's MFMAs overlap the other's softmax.
+// double-buffered LDS tile; one barrier per iteration.  Loads are never
+// predicated: rows past n re-read row n-1 and are masked.  Tiles that touch
+// the diagonal or the end of the sequence take a masked copy of the softmax;
+// the others a mask-free one.  Two waves per SIMD (<= 256 registers).
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -53,14 +75,12 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(
     float *__restrict__ lse, int Hq, int Hkv, int n, float sl2) {
     constexpr int KS = D / 16;
     constexpr int DT = D / 32;
-    constexpr int KPAD = D + 8;       // K tile row stride in halves (+16 B)
-    constexpr int VPAD = kBN + 4;     // V^T tile row stride in halves (+8 B)
-    constexpr int KLD = kBN * D / 8 / 256;        // uint4 K loads per thread
-    constexpr int VTOT = (kBN / 4) * (D / 8);     // 4-key x 8-channel V groups
-    constexpr int VLD = (VTOT + 255) / 256;       // V groups per thread
-    static_assert(KLD >= 1 && KLD * 256 * 8 == kBN * D, "K tile / threads");
+    constexpr int KPAD = D + 8;       // K row stride (halves): 4 dwords mod 64
+    constexpr int VSTR = D + 32;      // V row stride (halves): 16 dwords mod 32
+    constexpr int LD = kBN * D / 8 / 256;          // uint4 loads per thread
+    static_assert(LD >= 1 && LD * 256 * 8 == kBN * D, "tile / threads");
     __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kBN * KPAD];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_s[2][D * VPAD];
+    __shared__ __attribute__((aligned(16))) uint16_t v_s[2][kBN * VSTR];
 
     const int nqb = (n + kBM - 1) / kBM;
     const int qb = nqb - 1 - (int)blockIdx.x;       // longest rows first
@@ -79,12 +99,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(
 
     half8_t qf[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        if (qrow < n)
-            qf[ks] = load_h8(qp + (size_t)qrow * D + ks * 16 + 8 * hi);
-        else
-            qf[ks] = half8_t{};
-    }
+    for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = load_h8(qp + (size_t)min(qrow, n - 1) * D + ks * 16 + 8 * hi);
     float16_t oacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt] = float16_t{};
@@ -94,53 +110,96 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(
     const int kend = min(n, qb * kBM + kBM);
     const int ntiles = (kend + kBN - 1) / kBN;
 
-    uint4 kreg[KLD], vreg[VLD][4];
-    auto load_tile = [&](int k0) {
+    u32x4 kreg[LD], vreg[LD];
+    auto load_tile = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < KLD; ++i) {
+        for (int i = 0; i < LD; ++i) {
             const int idx = tid + 256 * i;
             const int r = idx / (D / 8), cc = idx % (D / 8);
-            kreg[i] = k0 + r < n ? *reinterpret_cast<const uint4 *>(
-                                       kp + (size_t)(k0 + r) * D + cc * 8)
-                                 : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < VLD; ++i) {
-            const int idx = tid + 256 * i;
-            const int kq4 = idx / (D / 8), dof = idx % (D / 8);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + 4 * kq4 + r;
-                vreg[i][r] = (idx < VTOT && key < n)
-                                 ? *reinterpret_cast<const uint4 *>(
-                                       vp + (size_t)key * D + dof * 8)
-                                 : make_uint4(0, 0, 0, 0);
-            }
+            const size_t off = (size_t)min(k0 + r, n - 1) * D + cc * 8;
+            kreg[i] = *reinterpret_cast<const u32x4 *>(kp + off);
+            vreg[i] = *reinterpret_cast<const u32x4 *>(vp + off);
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < KLD; ++i) {
+        for (int i = 0; i < LD; ++i) {
             const int idx = tid + 256 * i;
             const int r = idx / (D / 8), cc = idx % (D / 8);
-            *reinterpret_cast<uint4 *>(k_s[buf] + r * KPAD + cc * 8) = kreg[i];
+            *reinterpret_cast<u32x4 *>(k_s[buf] + r * KPAD + cc * 8) = kreg[i];
+            *reinterpret_cast<u32x4 *>(v_s[buf] + r * VSTR + cc * 8) = vreg[i];
         }
+    };
+
+    // lane-constant parts of the transposed V reads
+    const int grp = lane >> 4, L = lane & 15;
+    const int v_lane_off = (4 * (grp >> 1) + (L >> 2)) * VSTR + 16 * (grp & 1) + 4 * (L & 3);
+
+    auto tile_step = [&](auto MASKED, int buf, int k0) __attribute__((always_inline)) {
+        float16_t s[2];
 #pragma unroll
-        for (int i = 0; i < VLD; ++i) {
-            const int idx = tid + 256 * i;
-            const int kq4 = idx / (D / 8), dof = idx % (D / 8);
-            if (idx >= VTOT) break;
+        for (int st = 0; st < 2; ++st) {
+            s[st] = float16_t{};
 #pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                uint32_t h[4];
+            for (int ks = 0; ks < KS; ++ks) {
+                const half8_t a =
+                    load_h8(k_s[buf] + (st * 32 + l32) * KPAD + ks * 16 + 8 * hi);
+                s[st] = mfma32(a, qf[ks], s[st]);
+            }
+        }
+        // s[st][i] = S[key = k0 + 32 st + 8(i/4) + 4 hi + i%4][query = qrow]
+        if constexpr (decltype(MASKED)::value) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t w[4] = {vreg[i][r].x, vreg[i][r].y,
-                                           vreg[i][r].z, vreg[i][r].w};
-                    h[r] = (w[d >> 1] >> (16 * (d & 1))) & 0xffffu;
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = k0 + st * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+                    if (key > qrow || key >= n) s[st][i] = -INFINITY;
                 }
-                *reinterpret_cast<uint2 *>(vt_s[buf] + (dof * 8 + d) * VPAD + 4 * kq4) =
-                    make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(s[st][i], s[st][i + 1]));
+        tmax = fmaxf(tmax, shfl_xor(tmax, 32)) * sl2;
+        const float m_new = fmaxf(m_run, tmax);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        // rescale only when some row max of the wave moved
+        if (__ballot(m_new > m_run) != 0) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        }
+        m_run = m_new;
+
+        half8_t pf[4];                              // k-step (st, a2) = 2 st + a2
+        float l0 = 0.f, l1 = 0.f;                   // tile sum first: no drift
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][i], sl2, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][i + 1], sl2, -m_use));
+                l0 += p0;
+                l1 += p1;
+                pf[st * 2 + (i >> 3)][i & 7] = (half_t)p0;
+                pf[st * 2 + (i >> 3)][(i & 7) + 1] = (half_t)p1;
+            }
+        l_run += l0 + l1;
+        const uint16_t *vb = v_s[buf] + v_lane_off;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int st = kk >> 1, a2 = kk & 1;
+            const uint16_t *vk = vb + (st * 32 + 16 * a2) * VSTR;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const half4_t lo4 = ds_read_tr16(vk + dt * 32);
+                const half4_t hi4 = ds_read_tr16(vk + 8 * VSTR + dt * 32);
+                const half8_t a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3,
+                                                          4, 5, 6, 7);
+                oacc[dt] = mfma32(a, pf[kk], oacc[dt]);
             }
         }
     };
@@ -153,73 +212,11 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(
         const int k0 = kt * kBN;
         const bool more = kt + 1 < ntiles;
         if (more) load_tile(k0 + kBN);
-
         if (k0 <= q0 + 31) {                        // not fully masked
-            float16_t s[2];
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                s[st] = float16_t{};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const half8_t a =
-                        load_h8(k_s[buf] + (st * 32 + l32) * KPAD + ks * 16 + 8 * hi);
-                    s[st] = mfma32(a, qf[ks], s[st]);
-                }
-            }
-            // s[st][i] = S[key = k0 + 32 st + 8(i/4) + 4 hi + i%4][query = qrow]
-            const bool need_mask = (k0 + kBN - 1 > q0) || (k0 + kBN > n);
-            if (need_mask) {
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = k0 + st * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-                        if (key > qrow || key >= n) s[st][i] = -INFINITY;
-                    }
-            }
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[st][i]);
-            tmax = fmaxf(tmax, shfl_xor(tmax, 32)) * sl2;
-            const float m_new = fmaxf(m_run, tmax);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            // rescale only when some row max of the wave moved
-            if (__ballot(m_new > m_run) != 0) {
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-            }
-            m_run = m_new;
-
-            half8_t pf[4];                          // k-step (st, a2) = 2 st + a2
-            float l_tile = 0.f;                     // tile sum first: no drift
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(
-                        __builtin_fmaf(s[st][i], sl2, -m_use));
-                    l_tile += p;
-                    pf[st * 2 + (i >> 3)][i & 7] = (half_t)p;
-                }
-            l_run += l_tile;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int st = kk >> 1, a2 = kk & 1;
-                    const uint16_t *base = vt_s[buf] + (dt * 32 + l32) * VPAD + st * 32 +
-                                           16 * a2 + 4 * hi;
-                    const half4_t lo4 = *reinterpret_cast<const half4_t *>(base);
-                    const half4_t hi4 = *reinterpret_cast<const half4_t *>(base + 8);
-                    const half8_t a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3,
-                                                              4, 5, 6, 7);
-                    oacc[dt] = mfma32(a, pf[kk], oacc[dt]);
-                }
-            }
+            if ((k0 + kBN - 1 > q0) || (k0 + kBN > n))
+                tile_step(bool_c<true>{}, buf, k0);
+            else
+                tile_step(bool_c<false>{}, buf, k0);
         }
         if (more) store_tile(buf ^ 1);
         __syncthreads();
@@ -251,7 +248,9 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(
 // probabilities of its 16 query rows per 32-row sub-tile; the two lane halves
 // are combined once at the end.  The next 64-query tile (and its LSE) is
 // loaded into registers while the current one is used, into a double-buffered
-// LDS tile, with one barrier per tile.
+// LDS tile, with one barrier per tile.  Rows past n get LSE = +inf, so their
+// probabilities are exactly 0; only sub-tiles that cross the diagonal take
+// the masked copy of the update.
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -261,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
     constexpr int QPAD = D + 8;
     constexpr int QLD = kBQ2 * D / 8 / 256;         // uint4 loads per thread
     __shared__ __attribute__((aligned(16))) uint16_t q_s[2][kBQ2 * QPAD];
-    __shared__ float lse_s[2][kBQ2];
+    __shared__ __attribute__((aligned(16))) float lse_s[2][kBQ2];
 
     const int kb = blockIdx.x;                      // block 0 has most rows
     const int unit = blockIdx.y;                    // b * Hkv + kvh
@@ -276,12 +275,8 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
 
     half8_t kf[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        if (key < n)
-            kf[ks] = load_h8(kp + (size_t)key * D + ks * 16 + 8 * hi);
-        else
-            kf[ks] = half8_t{};
-    }
+    for (int ks = 0; ks < KS; ++ks)
+        kf[ks] = load_h8(kp + (size_t)min(key, n - 1) * D + ks * 16 + 8 * hi);
     // Column sum: each 64-row tile is summed on its own, then added to a
     // compensated (Kahan) running sum, so tens of thousands of small
     // probabilities added to a large column total do not drift low.
@@ -291,9 +286,9 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
     const int qstart = kb * kBK2;
     const int tiles_per_head = (n - qstart + kBQ2 - 1) / kBQ2;
     const int ntiles = g * tiles_per_head;
-    uint4 qreg[QLD];
+    u32x4 qreg[QLD];
     float lreg = 0.f;
-    auto load_tile = [&](int t) {
+    auto load_tile = [&](int t) __attribute__((always_inline)) {
         const int h = t / tiles_per_head;
         const int qt0 = qstart + (t % tiles_per_head) * kBQ2;
         const size_t bhq = (size_t)b * Hq + kvh * g + h;
@@ -302,21 +297,48 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
         for (int i = 0; i < QLD; ++i) {
             const int idx = tid + 256 * i;
             const int r = idx / (D / 8), cc = idx % (D / 8);
-            qreg[i] = qt0 + r < n ? *reinterpret_cast<const uint4 *>(
-                                        qp + (size_t)(qt0 + r) * D + cc * 8)
-                                  : make_uint4(0, 0, 0, 0);
+            qreg[i] = *reinterpret_cast<const u32x4 *>(
+                qp + (size_t)min(qt0 + r, n - 1) * D + cc * 8);
         }
-        if (tid < kBQ2)
-            lreg = (qt0 + tid < n) ? lse[bhq * n + qt0 + tid] * kLog2e : INFINITY;
+        if (tid < kBQ2) {
+            const float x = lse[bhq * n + min(qt0 + tid, n - 1)] * kLog2e;
+            lreg = qt0 + tid < n ? x : INFINITY;
+        }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < QLD; ++i) {
             const int idx = tid + 256 * i;
             const int r = idx / (D / 8), cc = idx % (D / 8);
-            *reinterpret_cast<uint4 *>(q_s[buf] + r * QPAD + cc * 8) = qreg[i];
+            *reinterpret_cast<u32x4 *>(q_s[buf] + r * QPAD + cc * 8) = qreg[i];
         }
         if (tid < kBQ2) lse_s[buf][tid] = lreg;
+    };
+
+    auto sub_tile = [&](auto MASKED, int buf, int qt0, int qs) __attribute__((always_inline)) -> float {
+        float16_t s = float16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const half8_t a =
+                load_h8(q_s[buf] + (qs * 32 + l32) * QPAD + ks * 16 + 8 * hi);
+            s = mfma32(a, kf[ks], s);
+        }
+        // s[i] = S[query = qt0 + 32 qs + 8(i/4) + 4 hi + i%4][key]
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const float4_t l4 = *reinterpret_cast<const float4_t *>(
+                &lse_s[buf][qs * 32 + 8 * i4 + 4 * hi]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * i4 + j], sl2, -l4[j]));
+                if constexpr (decltype(MASKED)::value) {
+                    if (qt0 + qs * 32 + 8 * i4 + 4 * hi + j < key) p = 0.f;
+                }
+                if (j & 1) t1 += p; else t0 += p;
+            }
+        }
+        return t0 + t1;
     };
 
     if (ntiles > 0) {
@@ -333,24 +355,10 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
             float tile = 0.f;
 #pragma unroll
             for (int qs = 0; qs < 2; ++qs) {
-                float16_t s = float16_t{};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const half8_t a =
-                        load_h8(q_s[buf] + (qs * 32 + l32) * QPAD + ks * 16 + 8 * hi);
-                    s = mfma32(a, kf[ks], s);
-                }
-                // s[i] = S[query = qt0 + 32 qs + 8(i/4) + 4 hi + i%4][key]
-                const int qb0 = qt0 + qs * 32;
-                const bool need_mask = (qb0 < k0w + 31) || (qb0 + 32 > n);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = qs * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    float p = __builtin_amdgcn_exp2f(
-                        __builtin_fmaf(s[i], sl2, -lse_s[buf][r]));
-                    if (need_mask && (qt0 + r < key || qt0 + r >= n)) p = 0.f;
-                    tile += p;
-                }
+                if (qt0 + qs * 32 < k0w + 31)       // crosses the diagonal
+                    tile += sub_tile(bool_c<true>{}, buf, qt0, qs);
+                else
+                    tile += sub_tile(bool_c<false>{}, buf, qt0, qs);
             }
             const float y = tile - colcomp;
             const float tt = colacc + y;
