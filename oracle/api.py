@@ -151,10 +151,10 @@ def pack_unit(k, v, sel, Gk, Gv):
     m = sel.size
     mp = (m // Gk) * Gk
     out = dict(
-        kq=np.zeros((mp // 16, D), np.uint32),
+        kq=np.zeros((mp, D // 16), np.uint32),
         ks=np.zeros((mp // Gk, D), np.uint16),
         kz=np.zeros((mp // Gk, D), np.uint16),
-        vq=np.zeros((mp, D // 16), np.uint32),
+        vq=np.zeros((mp // 16, D), np.uint32),
         vs=np.zeros((mp, D // Gv), np.uint16),
         vz=np.zeros((mp, D // Gv), np.uint16),
         kres=np.zeros((m - mp, D), np.uint16),
@@ -204,11 +204,11 @@ class OracleCache:
     """One layer's compressed cache for B x Hkv units, in the layout the
     oracle defines:
 
-      kq [B][Hkv][cap/16][D] uint32   word (w, c): tokens 16w..16w+15 of
-                                       channel c, token 16w+e at bits 2e..2e+1
+      kq [B][Hkv][cap][D/16] uint32   word (t, j): channels 16j..16j+15 of
+                                       token t, channel 16j+e at bits 2e..2e+1
       ks, kz [B][Hkv][cap/Gk][D]      fp16 bits, one per key group/channel
-      vq [B][Hkv][cap][D/16] uint32   word (t, j): channels 16j..16j+15 of
-                                       token t, channel 16j+e at bits 2e..
+      vq [B][Hkv][cap/16][D] uint32   word (w, c): tokens 16w..16w+15 of
+                                       channel c, token 16w+e at bits 2e..
       vs, vz [B][Hkv][cap][D/Gv]      fp16 bits, one per token/channel group
       kres, vres [B][Hkv][nr][D]      fp16 residual (KIVI streaming buffer)
     """
@@ -217,10 +217,10 @@ class OracleCache:
         assert capacity % Gk == 0 and residual_cap % Gk == 0
         self.B, self.Hkv, self.D, self.Gk, self.Gv = B, Hkv, D, Gk, Gv
         self.cap, self.nr = capacity, residual_cap
-        self.kq = np.zeros((B, Hkv, capacity // 16, D), np.uint32)
+        self.kq = np.zeros((B, Hkv, capacity, D // 16), np.uint32)
         self.ks = np.zeros((B, Hkv, capacity // Gk, D), np.uint16)
         self.kz = np.zeros_like(self.ks)
-        self.vq = np.zeros((B, Hkv, capacity, D // 16), np.uint32)
+        self.vq = np.zeros((B, Hkv, capacity // 16, D), np.uint32)
         self.vs = np.zeros((B, Hkv, capacity, D // Gv), np.uint16)
         self.vz = np.zeros_like(self.vs)
         self.kres = np.zeros((B, Hkv, residual_cap, D), np.uint16)
@@ -230,11 +230,11 @@ class OracleCache:
 
     def _store(self, b, h, at, out):
         Gk, D = self.Gk, self.D
-        mp = out["vq"].shape[0]
-        self.kq[b, h, at // 16:(at + mp) // 16] = out["kq"]
+        mp = out["kq"].shape[0]
+        self.kq[b, h, at:at + mp] = out["kq"]
         self.ks[b, h, at // Gk:(at + mp) // Gk] = out["ks"]
         self.kz[b, h, at // Gk:(at + mp) // Gk] = out["kz"]
-        self.vq[b, h, at:at + mp] = out["vq"]
+        self.vq[b, h, at // 16:(at + mp) // 16] = out["vq"]
         self.vs[b, h, at:at + mp] = out["vs"]
         self.vz[b, h, at:at + mp] = out["vz"]
         return mp

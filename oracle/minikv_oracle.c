@@ -341,17 +341,20 @@ int oracle_select(int n, const double *col, int n_hh, int n_recent,
 /* (sub-channel) and the per-token value quantisation; Fig. 1 caption: keys */
 /* per channel, values per token; [V] key_machinery: sixteen 2-bit codes    */
 /* per 32-bit word, fp16 scale and zero.                                    */
-/* reading (layout): keys are quantised per channel over groups of Gk       */
-/*   consecutive selected tokens; a key word holds 16 consecutive selected  */
-/*   tokens of one channel.  Values are quantised per token over groups of  */
-/*   Gv consecutive channels; a value word holds 16 consecutive channels of */
-/*   one token.  Element e of a word sits at bits 2e..2e+1.                 */
+/* reading (layout): the pages fix sixteen codes per 32-bit word but not   */
+/*   which sixteen.  Keys are quantised per channel over groups of Gk       */
+/*   consecutive selected tokens; a key word holds 16 consecutive channels  */
+/*   of one token.  Values are quantised per token over groups of Gv        */
+/*   consecutive channels; a value word holds 16 consecutive selected       */
+/*   tokens of one channel.  Each word thus runs along the dimension that   */
+/*   attention sums over (channels for q.k, tokens for p.v).  Element e of  */
+/*   a word sits at bits 2e..2e+1.                                          */
 /* reading (ragged tail): the first floor(m / Gk) * Gk selected tokens are  */
 /*   packed; the last m mod Gk stay in fp16 as the start of the residual.   */
 /*                                                                          */
 /*   k, v          [n][D] fp16 of this unit; sel[m] ascending indices       */
-/*   kq  [mp/16][D] uint32;  ks, kz [mp/Gk][D] fp16                         */
-/*   vq  [mp][D/16] uint32;  vs, vz [mp][D/Gv] fp16                         */
+/*   kq  [mp][D/16] uint32;  ks, kz [mp/Gk][D] fp16                         */
+/*   vq  [mp/16][D] uint32;  vs, vz [mp][D/Gv] fp16                         */
 /*   kres, vres [m - mp][D] fp16                                            */
 /* Returns mp (number of packed tokens) or -1 on bad arguments.             */
 /* ------------------------------------------------------------------------ */
@@ -368,7 +371,7 @@ int oracle_pack_unit(int D, int Gk, int Gv, const uint16_t *k,
     uint16_t *x = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(Gk > Gv ? Gk : Gv));
     uint8_t *codes = (uint8_t *)malloc((size_t)(Gk > Gv ? Gk : Gv));
 
-    memset(kq, 0, sizeof(uint32_t) * (size_t)(mp / 16) * D);
+    memset(kq, 0, sizeof(uint32_t) * (size_t)mp * (D / 16));
     for (int gi = 0; gi < mp / Gk; ++gi) {
         for (int c = 0; c < D; ++c) {
             for (int t = 0; t < Gk; ++t)
@@ -377,12 +380,12 @@ int oracle_pack_unit(int D, int Gk, int Gv, const uint16_t *k,
                                &kz[(long)gi * D + c]);
             for (int t = 0; t < Gk; ++t) {
                 int p = gi * Gk + t;
-                kq[(long)(p / 16) * D + c] |= (uint32_t)codes[t] << (2 * (p % 16));
+                kq[(long)p * (D / 16) + c / 16] |= (uint32_t)codes[t] << (2 * (c % 16));
             }
         }
     }
 
-    memset(vq, 0, sizeof(uint32_t) * (size_t)mp * (D / 16));
+    memset(vq, 0, sizeof(uint32_t) * (size_t)(mp / 16) * D);
     for (int p = 0; p < mp; ++p) {
         const uint16_t *row = v + (long)sel[p] * D;
         for (int G = 0; G < D / Gv; ++G) {
@@ -391,7 +394,7 @@ int oracle_pack_unit(int D, int Gk, int Gv, const uint16_t *k,
                                &vz[(long)p * (D / Gv) + G]);
             for (int i = 0; i < Gv; ++i) {
                 int c = G * Gv + i;
-                vq[(long)p * (D / 16) + c / 16] |= (uint32_t)codes[i] << (2 * (c % 16));
+                vq[(long)(p / 16) * D + c] |= (uint32_t)codes[i] << (2 * (p % 16));
             }
         }
     }
@@ -435,10 +438,10 @@ int oracle_decode_unit(int D, int g, int Gk, int Gv, const uint16_t *q,
     double *s = (double *)malloc(sizeof(double) * (size_t)T);
     for (int t = 0; t < n_packed; ++t) {
         for (int c = 0; c < D; ++c) {
-            int kc = (int)((kq[(long)(t / 16) * D + c] >> (2 * (t % 16))) & 3u);
+            int kc = (int)((kq[(long)t * (D / 16) + c / 16] >> (2 * (c % 16))) & 3u);
             long km = (long)(t / Gk) * D + c;
             kh[(long)t * D + c] = (double)oracle_dequant(kc, ks[km], kz[km]);
-            int vc = (int)((vq[(long)t * (D / 16) + c / 16] >> (2 * (c % 16))) & 3u);
+            int vc = (int)((vq[(long)(t / 16) * D + c] >> (2 * (t % 16))) & 3u);
             long vm = (long)t * (D / Gv) + c / Gv;
             vh[(long)t * D + c] = (double)oracle_dequant(vc, vs[vm], vz[vm]);
         }

@@ -2,8 +2,9 @@
 
 - Word layout: groups built so their codes are known in advance (exact
   arithmetic progressions) must produce the words an independent shift-and-or
-  in this test builds from those codes -- keys along tokens, values along
-  channels, element e at bits 2e..2e+1.
+  in this test builds from those codes -- key words along channels (16
+  channels of one token), value words along tokens (16 tokens of one
+  channel), element e at bits 2e..2e+1.
 - Ragged tail: the last m mod Gk selected tokens land, unchanged, in the fp16
   residual.
 - Flush: appending residual_cap tokens packs exactly what pack() of those
@@ -22,18 +23,20 @@ from bit_quantized_attention_two_amd import synth
 
 def _unpack_keys(kq, ks, kz, n_packed, Gk):
     """Independent numpy unpacker for key words -> fp32 values [n][D]."""
-    D = kq.shape[-1]
+    D = kq.shape[-1] * 16
+    c = np.arange(D)
+    codes = (kq[:n_packed][:, c // 16] >> (2 * (c % 16)).astype(np.uint32)) & 3
     t = np.arange(n_packed)
-    codes = (kq[t // 16, :] >> (2 * (t % 16))[:, None].astype(np.uint32)) & 3
     s = ks[t // Gk].view(np.float16).astype(np.float32)
     z = kz[t // Gk].view(np.float16).astype(np.float32)
     return codes.astype(np.float32) * s + z
 
 
 def _unpack_values(vq, vs, vz, n_packed, Gv):
-    D = vq.shape[-1] * 16
+    D = vq.shape[-1]
+    t = np.arange(n_packed)
+    codes = (vq[t // 16, :] >> (2 * (t % 16))[:, None].astype(np.uint32)) & 3
     c = np.arange(D)
-    codes = (vq[:n_packed][:, c // 16] >> (2 * (c % 16)).astype(np.uint32)) & 3
     s = vs[:n_packed][:, c // Gv].view(np.float16).astype(np.float32)
     z = vz[:n_packed][:, c // Gv].view(np.float16).astype(np.float32)
     return codes.astype(np.float32) * s + z
@@ -53,12 +56,12 @@ def test_pack_word_layout_known_codes(oracle):
     v = (codes_v * 0.25 + 2.0).astype(np.float16)
     sel = np.arange(n, dtype=np.int32)
     out = oracle.pack_unit(k, v, sel, Gk, Gv)
-    kq = np.zeros((n // 16, D), np.uint32)
-    for t in range(n):
-        kq[t // 16] |= (codes_k[t].astype(np.uint32) << (2 * (t % 16)))
-    vq = np.zeros((n, D // 16), np.uint32)
+    kq = np.zeros((n, D // 16), np.uint32)
     for c in range(D):
-        vq[:, c // 16] |= (codes_v[:, c].astype(np.uint32) << (2 * (c % 16)))
+        kq[:, c // 16] |= (codes_k[:, c].astype(np.uint32) << (2 * (c % 16)))
+    vq = np.zeros((n // 16, D), np.uint32)
+    for t in range(n):
+        vq[t // 16] |= (codes_v[t].astype(np.uint32) << (2 * (t % 16)))
     assert np.array_equal(out["kq"], kq)
     assert np.array_equal(out["vq"], vq)
     assert np.all(out["ks"].view(np.float16) == 0.25)
@@ -74,7 +77,7 @@ def test_pack_gather_and_ragged_tail(oracle, Gk):
     sel = synth.gen_selection(5, 1, n, 75)[0]
     out = oracle.pack_unit(k[0], v[0], sel, Gk, Gv)
     mp = (75 // Gk) * Gk
-    assert out["vq"].shape[0] == mp
+    assert out["kq"].shape[0] == mp
     assert np.array_equal(out["kres"], k[0][sel[mp:]].view(np.uint16))
     assert np.array_equal(out["vres"], v[0][sel[mp:]].view(np.uint16))
     # gather: packing sel equals packing the gathered rows with identity
@@ -104,9 +107,9 @@ def test_append_flush_equals_pack(oracle):
     assert (cache.n_packed, cache.n_res) == (64, 0)
     ref = oracle.pack_unit(k[0, 1, 32:64], v[0, 1, 32:64],
                            np.arange(32, dtype=np.int32), Gk, Gv)
-    assert np.array_equal(cache.kq[0, 1, 2:4], ref["kq"])
+    assert np.array_equal(cache.kq[0, 1, 32:64], ref["kq"])
     assert np.array_equal(cache.ks[0, 1, 2:4], ref["ks"])
-    assert np.array_equal(cache.vq[0, 1, 32:64], ref["vq"])
+    assert np.array_equal(cache.vq[0, 1, 2:4], ref["vq"])
     assert np.array_equal(cache.vz[0, 1, 32:64], ref["vz"])
     for t in range(64, 96):
         cache.append(k[:, :, t], v[:, :, t])
