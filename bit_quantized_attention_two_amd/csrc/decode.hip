@@ -3,32 +3,38 @@
 // Verdict record for MiniKV (arXiv 2411.18077), forward implications: the
 // selection is fixed after prefill, so the retained cache has a fixed layout
 // and decoding can dequantise inside the attention kernel.  This kernel never
-// materialises fp16 keys or values: it works in the code domain.
+// materialises fp16 keys or values; both contractions run on the matrix
+// cores in the code domain:
 //
-//   logit(t) = sum_c q'_c (code_kc * s_k + z_k)
-//            = sum_c (q'_c s_k[g,c]) code_kc + sum_c q'_c z_k[g,c]
-//   o_c      = sum_t p_t (code_vc * s_v[t,G] + z_v[t,G])
-//            = sum_t (p_t s_v[t,G]) code_vc + sum_t p_t z_v[t,G]
+//   logit(t) = sum_c q_c (code_tc s_k[g(t),c] + z_k[g(t),c])
+//            = sum_c code_tc (q_c s_k[g,c])   +   sum_c q_c z_k[g,c]
+//   o_c      = sum_t p_t (code_tc s_v[t,G(c)] + z_v[t,G(c)])
+//            = sum_t code_tc (p_t s_v[t,G])   +   sum_t p_t z_v[t,G]
 //
-// with q' = q log2(e) / sqrt(D) so that the softmax uses exp2.  The products
-// q' s (per key group and channel) and p s (per token and channel group) are
-// formed once and reused for the 16 codes of a word; all g query heads of a
-// kv head share each read of its codes.
+// Codes as MFMA operands.  A key word holds 16 channels of one token and a
+// value word 16 tokens of one channel, both along the summed dimension.
+// Masking a word with 0x00030003 << 2i leaves two 2-bit fields in the
+// mantissas of two fp16 halves: the subnormals code * 4^i * 2^-24, exact.
+// The matching weights (q s for keys, p s for values) are scaled by 4^-i and
+// split into two fp16 parts hi + lo, which hold the fp32 weight to about 22
+// bits; each product code * weight is exact in the fp32 accumulator.  So the
+// only rounding is the fp32 accumulation, as in a plain fp32 dot product.
+// Every fp16 operand stays within range: q is scaled by a power of two to
+// |q| < 1 per head, p <= 1, and a scale is at most 65504 * 2 / 3.
+//
+// The per-group scale s_k[g, c] makes the key weights differ per key group.
+// One 16-column B operand holds the weights of (head, group) pairs for 16/g
+// groups at once; a 16-token tile multiplies it and keeps the columns of its
+// own group.  The value weights use columns (head, channel group); each
+// channel row keeps the column of its own group.  The z terms: per key
+// group an MFMA of the zero-points with q, and per token a VALU sum.
 //
 // Work split: block (split, unit) covers `chunk` packed tokens of one unit,
 // each of its 4 waves a quarter of them; the last split of a unit is its
-// fp16 residual when it has one.  A wave computes its logits (the 16 lanes
-// of a 16-token key row split the channels), its own softmax statistics and
-// its P.V; the block merges its waves in LDS and writes one partial
-// (max, sum, unnormalised o) to the workspace.  A second kernel merges the
-// partials of each (unit, head) and writes o.  (Merging in the last block to
-// finish would need device-scope fences, which on this multi-die part write
-// back and invalidate the L2 of every block that takes them.)
-//
-// Latency: every global load is issued ahead of its use and never predicated
-// off (indices are clamped; extra rows get weight 0).  The first batch of
-// value rows is requested at kernel start together with the key rows, the
-// next key row and value batch while the current ones are used.
+// fp16 residual when it has one.  A wave computes all its logits (phase K),
+// its softmax statistics, then P.V (phase V); the block merges its waves in
+// LDS and writes one partial (max, sum, unnormalised o) to the workspace.
+// A second kernel merges the partials of each (unit, head) and writes o.
 //
 // Fused append: when the caller passes a new token, the residual block reads
 // it from the call's input, uses it as residual slot `new_slot`, and stores
@@ -44,7 +50,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kMinWaveChunk = 64;
-constexpr int kMaxWaveChunk = 512;
+constexpr int kMaxWaveChunk = 256;
 constexpr int kMaxSplit = 512;
 
 struct DecArgs {
@@ -58,6 +64,14 @@ struct DecArgs {
     float *part_ml;                  // [units][nsplit][G][2]
     float *part_o;                   // [units][nsplit][G][D]
 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16x16x32 fp16 MFMA: A lane l holds A[l%16][8(l/16)+j], B lane l holds
+// B[8(l/16)+j][l%16], C lane l register i holds C[4(l/16)+i][l%16].
+__device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -73,224 +87,575 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp<0x121>(v);       // row_ror:1
     return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, shfl_xor(v, off));
-    return v;
-}
 __device__ __forceinline__ float wave_sum(float v) {
     for (int off = 32; off > 0; off >>= 1) v += shfl_xor(v, off);
     return v;
 }
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+}
+
+// The two code fields of dword i of a shifted word, as fp16 subnormals
+// code * 4^i * 2^-24 in the low and high half.
+__device__ __forceinline__ half8_t code_operand(uint32_t x) {
+    const u32x4 v = {x & 0x00030003u, x & 0x000c000cu, x & 0x00300030u,
+                     x & 0x00c000c0u};
+    return __builtin_bit_cast(half8_t, v);
+}
+
+// fp16 hi + lo of a weight (hi rounded to nearest, lo the rounded rest).
+__device__ __forceinline__ void split2(float w, half_t &hi, half_t &lo) {
+    hi = (half_t)w;
+    lo = (half_t)(w - (float)hi);
+}
+
 __device__ __forceinline__ void unpack8h(uint4 x, float *f) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = h2f((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
 }
-// N consecutive fp16 values (N = 4 or 8) -> fp32.
-template <int N>
-__device__ __forceinline__ void load_halves(const uint16_t *p, float *f) {
-    if constexpr (N == 8) {
-        unpack8h(*reinterpret_cast<const uint4 *>(p), f);
-    } else {
-        const uint2 x = *reinterpret_cast<const uint2 *>(p);
-        const uint32_t w[2] = {x.x, x.y};
+
+// Per-wave LDS.  `ls` holds the logits of the wave's tokens, then their
+// probabilities times 4^-(t%4), [h][t]; at the end, aliased, the wave's
+// unnormalised output [h][D].  `sv` / `zv` hold the value scales and
+// zero-points per 16-channel group and token, [g16][t] (a value group of
+// more than 16 channels repeats its scale in each of its 16-channel parts).
+// Row strides are padded so that rows read by different lanes fall in
+// different LDS banks.
+constexpr int kLsStride = kMaxWaveChunk + 4;      // floats
+constexpr int kSvStride = kMaxWaveChunk + 8;      // halves
+template <int D, int G>
+struct alignas(16) WaveLds {
+    static constexpr int NG16 = D / 16;
+    float ls[G * kLsStride];
+    half_t sv[NG16 * kSvStride];
+    half_t zv[NG16 * kSvStride];
+    float bias[16 * G];                           // key z terms [group][h]
+};
+
+// ------------------------------------------------------ packed tokens
+// Tokens [t0, t0 + nt) of the packed region; t0 and nt are multiples of Gk
+// and of 16, nt <= kMaxWaveChunk.
+//
+// Phase K: all logits of the wave's tokens, in batches of 64 (four 16-token
+// tiles); the key words of the next batch are loaded while a batch is
+// multiplied.  Softmax: the wave's maxima, the probabilities and the value
+// meta are staged in LDS.  Phase V: NPASS passes over the value channels;
+// pass P covers 16-channel groups [P*GPP, (P+1)*GPP) for every head, so its
+// 16 B-operand columns are exactly the (head, group) pairs its rows need.
+template <int D, int G, bool FULLV>
+__device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
+                                            int nt, WaveLds<D, G> &L,
+                                            float *m_out, float *l_out) {
+    constexpr int KB = D / 32;                    // key k-blocks
+    constexpr int KW = D / 16;                    // key words per token
+    constexpr int NG16 = D / 16;                  // 16-channel value groups
+    constexpr int NG = 16 / G;                    // key groups per B operand
+    constexpr int BT = G == 8 ? 32 : 64;          // tokens per key batch (within one key operand: 256 / G >= BT)
+    constexpr int TPB = BT / 16;                  // key tiles per batch
+    constexpr int NPASS = (G * NG16 + 15) / 16;   // value passes
+    constexpr int GPP = NG16 / NPASS;             // value groups per pass
+    constexpr int MBP = GPP;                      // row blocks per pass
+    constexpr int CP = D / NPASS;                 // channels per pass
+    const CacheView &c = a.c;
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, qd = lane >> 4;
+    const int Gk = c.Gk;
+    const int NGV = D / c.Gv;                     // stored value groups
+    const uint16_t *qu = a.q + (size_t)unit * G * D;
+    const uint32_t *kq = reinterpret_cast<const uint32_t *>(c.kq) +
+                         (size_t)unit * c.kq_unit();
+    const uint16_t *ks = c.ks + (size_t)unit * c.km_unit();
+    const uint16_t *kz = c.kz + (size_t)unit * c.km_unit();
+    const uint32_t *vq = reinterpret_cast<const uint32_t *>(c.vq) +
+                         (size_t)unit * c.vq_unit();
+    const uint16_t *vs = c.vs + (size_t)unit * c.vm_unit();
+    const uint16_t *vz = c.vz + (size_t)unit * c.vm_unit();
+    const int g_first = t0 / Gk;
+    const int n_grp = nt / Gk;
+    const int nbatch = (nt + BT - 1) / BT;
+    const int bblk = NG * Gk;                     // tokens per key B operand
+    const int last = (nbatch - 1) * BT;           // start of the last batch
+
+    // ---- key B operand columns: column r = (group r / G of the operand,
+    // head r % G); k-slot (i, hf) of k-block kb is channel
+    // 16 w + 4 (qd & 1) + i + 8 hf with w = (qd >> 1) KB + kb.
+    const int hk = r % G;
+    const int gcol = r / G;
+
+    // ---- this lane's q channels as fp16 pairs (hf = 0, 1) per (kb, i), in
+    // the k-slot order of the key operands; and the power of two
+    // 2^e > max |q_h| per head.
+    uint32_t qh[KB][4];
+    float qmax = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = h2f((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
+    for (int kb = 0; kb < KB; ++kb) {
+        const int w = (qd >> 1) * KB + kb;
+        const uint2 x0 = *reinterpret_cast<const uint2 *>(
+            qu + (size_t)hk * D + 16 * w + 4 * (qd & 1));
+        const uint2 x1 = *reinterpret_cast<const uint2 *>(
+            qu + (size_t)hk * D + 16 * w + 4 * (qd & 1) + 8);
+        const uint32_t a0[2] = {x0.x, x0.y}, a1[2] = {x1.x, x1.y};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = (a0[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+            const uint32_t hi = (a1[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+            qh[kb][i] = lo | (hi << 16);
+            qmax = fmaxf(qmax, fmaxf(fabsf(h2f((uint16_t)lo)), fabsf(h2f((uint16_t)hi))));
+        }
     }
-}
-// N consecutive 32-bit words (N = 4 or 8).
-template <int N>
-__device__ __forceinline__ void load_words(const uint32_t *p, uint32_t *w) {
-    const uint4 a = reinterpret_cast<const uint4 *>(p)[0];
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-    if constexpr (N == 8) {
-        const uint4 b = reinterpret_cast<const uint4 *>(p)[1];
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    qmax = fmaxf(qmax, shfl_xor(qmax, 16));
+    qmax = fmaxf(qmax, shfl_xor(qmax, 32));
+    const int qe = __builtin_amdgcn_frexp_expf(qmax);
+    // logit (log2 units) = (acc * 2^(24 + e) + z term) * qscale
+    const float kfac = __builtin_amdgcn_ldexpf(a.qscale, 24 + qe);
+
+    // ---- loaders (indices clamped, never predicated)
+    uint2 ksr[KB][2];                             // key scales of a B operand
+    auto load_kscale = [&](int tok) {             // B operand holding tok
+        const int gs = g_first + min((tok / bblk) * NG + gcol, n_grp - 1);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int w = (qd >> 1) * KB + kb;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                ksr[kb][hf] = *reinterpret_cast<const uint2 *>(
+                    ks + (size_t)gs * D + 16 * w + 4 * (qd & 1) + 8 * hf);
+        }
+    };
+    uint2 kzr[KB][2];                             // key zeros, rows = groups
+    auto load_kzero = [&](int tok) {
+        const int gz = g_first + min((tok / bblk) * NG + r, n_grp - 1);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int w = (qd >> 1) * KB + kb;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                kzr[kb][hf] = *reinterpret_cast<const uint2 *>(
+                    kz + (size_t)gz * D + 16 * w + 4 * (qd & 1) + 8 * hf);
+        }
+    };
+    uint32_t kw[TPB][KB];                         // key words of a batch
+    auto load_kwords = [&](int tok) {
+#pragma unroll
+        for (int j = 0; j < TPB; ++j) {
+            const int t = min(tok + 16 * j + r, nt - 1);
+            const uint32_t *wp = kq + (size_t)(t0 + t) * KW + (qd >> 1) * KB;
+            if constexpr (KB == 4) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(wp);
+                kw[j][0] = x.x; kw[j][1] = x.y; kw[j][2] = x.z; kw[j][3] = x.w;
+            } else {
+                const uint2 x = *reinterpret_cast<const uint2 *>(wp);
+                kw[j][0] = x.x; kw[j][1] = x.y;
+            }
+        }
+    };
+
+    // key weights (B operand) from the scales in ksr
+    half8_t bhi[KB], blo[KB];
+    auto build_b = [&]() {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const uint32_t sx[2][2] = {{ksr[kb][0].x, ksr[kb][0].y},
+                                       {ksr[kb][1].x, ksr[kb][1].y}};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const float sc = h2f((uint16_t)(sx[hf][i >> 1] >> (16 * (i & 1))));
+                    const float qv = h2f((uint16_t)(qh[kb][i] >> (16 * hf)));
+                    half_t h_, l_;
+                    split2(__builtin_amdgcn_ldexpf(qv * sc, -qe - 2 * i), h_, l_);
+                    bhi[kb][2 * i + hf] = h_;
+                    blo[kb][2 * i + hf] = l_;
+                }
+        }
+    };
+    // z terms of the operand's groups (rows) for every head (columns), in
+    // log2 units, with the key operands' channel order on both sides
+    auto build_bias = [&]() {
+        float4_t cb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const u32x4 zb = {(kzr[kb][0].x & 0xffffu) | (kzr[kb][1].x << 16),
+                              (kzr[kb][0].x >> 16) | (kzr[kb][1].x & 0xffff0000u),
+                              (kzr[kb][0].y & 0xffffu) | (kzr[kb][1].y << 16),
+                              (kzr[kb][0].y >> 16) | (kzr[kb][1].y & 0xffff0000u)};
+            const u32x4 qv = {qh[kb][0], qh[kb][1], qh[kb][2], qh[kb][3]};
+            cb = mfma16(__builtin_bit_cast(half8_t, zb), __builtin_bit_cast(half8_t, qv), cb);
+        }
+        if (r < G)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) L.bias[(4 * qd + i) * G + r] = cb[i] * a.qscale;
+    };
+
+    // ============================================================ phase K
+    load_kscale(0);
+    load_kzero(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_kwords(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (G == 1) {                       // 16 groups cover the wave
+        build_b();
+        build_bias();
+        wave_lds_sync();
+    }
+    float mloc = -INFINITY;
+    for (int b = 0; b < nbatch; ++b) {
+        const int tok = b * BT;                   // wave-relative
+        const int nxt = min(tok + BT, last);      // next batch (clamped)
+        if constexpr (G > 1) {
+            if (tok % bblk == 0) {                // a new key operand
+                build_b();
+                build_bias();
+                wave_lds_sync();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_kscale(nxt);
+            load_kzero(nxt);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int gb = (tok / bblk) * NG;         // first group of the operand
+#pragma unroll
+        for (int j = 0; j < TPB; ++j) {
+            // tiles past the end use clamped rows and are never read
+            const int tl = min(tok + 16 * j, nt - 16);
+            float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const half8_t av = code_operand(kw[j][kb] >> (8 * (qd & 1)));
+                acc = mfma16(av, bhi[kb], acc);
+                acc = mfma16(av, blo[kb], acc);
+            }
+            if (gcol == tl / Gk - gb && tok + 16 * j < nt) {
+                const float bz = L.bias[(tl / Gk - gb) * G + hk];
+                float4_t lg;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lg[i] = __builtin_fmaf(acc[i], kfac, bz);
+                    mloc = fmaxf(mloc, lg[i]);
+                }
+                *reinterpret_cast<float4_t *>(&L.ls[hk * kLsStride + tok + 16 * j + 4 * qd]) = lg;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_kwords(nxt);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ================================================== softmax, staging
+    for (int off = G; off < 64; off <<= 1) mloc = fmaxf(mloc, shfl_xor(mloc, off));
+    float m_h[G], l_h[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m_h[h] = __shfl(mloc, h, 64);
+        l_h[h] = 0.f;
+    }
+    wave_lds_sync();
+    const int nt32 = (nt + 31) & ~31;
+    for (int t = lane; t < nt32; t += 64) {
+        const bool ok = t < nt;
+        const size_t row = (size_t)(t0 + min(t, nt - 1)) * NGV;
+        half_t sg[NG16], zg[NG16];
+        if constexpr (FULLV && NG16 == 8) {
+            const half8_t s8 = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4 *>(vs + row));
+            const half8_t z8 = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4 *>(vz + row));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { sg[j] = s8[j]; zg[j] = z8[j]; }
+        } else if constexpr (FULLV) {
+            const half4_t s4 = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(vs + row));
+            const half4_t z4 = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(vz + row));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { sg[j] = s4[j]; zg[j] = z4[j]; }
+        } else {
+            // value groups of Gv > 16 channels: repeat per 16-channel part
+            const int per = NG16 / NGV;
+#pragma unroll
+            for (int j = 0; j < NG16; ++j) {
+                sg[j] = __builtin_bit_cast(half_t, vs[row + j / per]);
+                zg[j] = __builtin_bit_cast(half_t, vz[row + j / per]);
+            }
+        }
+        const float q4 = __builtin_amdgcn_ldexpf(1.f, -2 * (t & 3));
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float p = ok ? __builtin_amdgcn_exp2f(L.ls[h * kLsStride + t] - m_h[h]) : 0.f;
+            l_h[h] += p;
+            L.ls[h * kLsStride + t] = p * q4;
+        }
+#pragma unroll
+        for (int j = 0; j < NG16; ++j) {
+            L.sv[j * kSvStride + t] = ok ? sg[j] : (half_t)0.f;
+            L.zv[j * kSvStride + t] = ok ? zg[j] : (half_t)0.f;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) l_h[h] = wave_sum(l_h[h]);
+    wave_lds_sync();
+
+    // ============================================================ phase V
+    // token slots of this lane in a 32-token step: tb + i, tb + 8 + i
+    const int tb = 16 * (qd >> 1) + 4 * (qd & 1);
+    const int last_blk = (t0 + nt) / 16 - 1;
+    float4_t outv[NPASS][MBP];                    // kept columns, see below
+    float zsum[NPASS];
+#pragma unroll
+    for (int P = 0; P < NPASS; ++P) {
+        // column r of this pass = (head r / GPP, group P GPP + r % GPP)
+        const int hc = min(r / GPP, G - 1);
+        const int vg = P * GPP + r % GPP;
+        float4_t acc[MBP];
+#pragma unroll
+        for (int mb = 0; mb < MBP; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+        float za[4] = {0.f, 0.f, 0.f, 0.f};
+        // value words: channels P CP + r MBP + mb of a 16-token block
+        uint32_t vw[MBP];
+        auto load_vw = [&](int st) {
+            const int blk = min((t0 + st) / 16 + (qd >> 1), last_blk);
+            const uint32_t *wp = vq + (size_t)blk * D + P * CP + r * MBP;
+            if constexpr (MBP == 8) {
+                const uint4 x0 = *reinterpret_cast<const uint4 *>(wp);
+                const uint4 x1 = *reinterpret_cast<const uint4 *>(wp + 4);
+                vw[0] = x0.x; vw[1] = x0.y; vw[2] = x0.z; vw[3] = x0.w;
+                vw[4] = x1.x; vw[5] = x1.y; vw[6] = x1.z; vw[7] = x1.w;
+            } else if constexpr (MBP == 4) {
+                const uint4 x0 = *reinterpret_cast<const uint4 *>(wp);
+                vw[0] = x0.x; vw[1] = x0.y; vw[2] = x0.z; vw[3] = x0.w;
+            } else if constexpr (MBP == 2) {
+                const uint2 x0 = *reinterpret_cast<const uint2 *>(wp);
+                vw[0] = x0.x; vw[1] = x0.y;
+            } else {
+                vw[0] = wp[0];
+            }
+        };
+        load_vw(0);
+        for (int st = 0; st < nt32; st += 32) {
+            half8_t av[MBP];
+#pragma unroll
+            for (int mb = 0; mb < MBP; ++mb) av[mb] = code_operand(vw[mb] >> (8 * (qd & 1)));
+            __builtin_amdgcn_sched_barrier(0);
+            load_vw(min(st + 32, nt32 - 32));
+            __builtin_amdgcn_sched_barrier(0);
+            const float *pp = &L.ls[hc * kLsStride + st + tb];
+            const half_t *sp = &L.sv[vg * kSvStride + st + tb];
+            const half_t *zp = &L.zv[vg * kSvStride + st + tb];
+            const float4_t p0 = *reinterpret_cast<const float4_t *>(pp);
+            const float4_t p1 = *reinterpret_cast<const float4_t *>(pp + 8);
+            const half4_t s0 = *reinterpret_cast<const half4_t *>(sp);
+            const half4_t s1 = *reinterpret_cast<const half4_t *>(sp + 8);
+            const half4_t z0 = *reinterpret_cast<const half4_t *>(zp);
+            const half4_t z1 = *reinterpret_cast<const half4_t *>(zp + 8);
+            half8_t bh, bl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                half_t h0, l0, h1, l1;
+                split2(p0[i] * (float)s0[i], h0, l0);
+                split2(p1[i] * (float)s1[i], h1, l1);
+                bh[2 * i] = h0; bh[2 * i + 1] = h1;
+                bl[2 * i] = l0; bl[2 * i + 1] = l1;
+                // p is stored times 4^-i: keep one z sum per i
+                za[i] += p0[i] * (float)z0[i] + p1[i] * (float)z1[i];
+            }
+#pragma unroll
+            for (int mb = 0; mb < MBP; ++mb) {
+                acc[mb] = mfma16(av[mb], bh, acc[mb]);
+                acc[mb] = mfma16(av[mb], bl, acc[mb]);
+            }
+        }
+        float zt = za[0] + __builtin_amdgcn_ldexpf(za[1], 2) +
+                   __builtin_amdgcn_ldexpf(za[2], 4) + __builtin_amdgcn_ldexpf(za[3], 6);
+        zt += shfl_xor(zt, 16);
+        zt += shfl_xor(zt, 32);
+#pragma unroll
+        for (int mb = 0; mb < MBP; ++mb) outv[P][mb] = acc[mb];
+        zsum[P] = zt;
+    }
+    wave_lds_sync();
+    // keep, for each channel row, the column of its own group; the wave's
+    // output [h][D] overwrites its probabilities
+    float *out = L.ls;
+#pragma unroll
+    for (int P = 0; P < NPASS; ++P) {
+        if (r < G * GPP) {
+            const int h = r / GPP, vg = P * GPP + r % GPP;
+#pragma unroll
+            for (int mb = 0; mb < MBP; ++mb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ch = P * CP + (4 * qd + i) * MBP + mb;
+                    if (ch / 16 == vg)
+                        out[h * D + ch] = __builtin_fmaf(outv[P][mb][i], 16777216.f, zsum[P]);
+                }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m_out[h] = m_h[h];
+        l_out[h] = l_h[h];
     }
 }
 
+// ------------------------------------------------------ fp16 residual
+// Tokens [t0, t0 + nt) of the residual, 1 <= nt <= 64.  Logits: 16 lanes
+// per token (D/16 channels each), four tokens per pass; P.V: the same lanes
+// over the same passes, the four token phases summed at the end.  The loads
+// of a batch of passes are all issued before their first use.
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
-    constexpr int WPT = D / 16;               // value words per token
-    constexpr int TS = 64 / WPT;              // tokens per V pass of a wave
-    constexpr int MAXW = kMaxWaveChunk * G <= 1024 ? kMaxWaveChunk : 1024 / G;
-    constexpr int VB = G <= 2 ? 8 : 4;        // value rows per load batch
+__device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0,
+                                              int nt, WaveLds<D, G> &L,
+                                              float *m_out, float *l_out) {
+    constexpr int CPL = D / 16;                   // channels per lane
+    constexpr int PB = 8;                         // passes per load batch
+    const CacheView &c = a.c;
+    const int lane = threadIdx.x & 63;
+    const int part = lane & 15, ph = lane >> 4;
+    const uint16_t *qu = a.q + (size_t)unit * G * D;
+    const uint16_t *kr = c.kres + (size_t)unit * c.res_unit();
+    const uint16_t *vr = c.vres + (size_t)unit * c.res_unit();
+    const uint16_t *kn = a.k_new ? a.k_new + (size_t)unit * D : nullptr;
+    const uint16_t *vn = a.v_new ? a.v_new + (size_t)unit * D : nullptr;
+    auto row_ptr = [&](const uint16_t *res, const uint16_t *nw, int slot) {
+        return (nw && slot == a.new_slot) ? nw : res + (size_t)slot * D;
+    };
+    auto load_row = [&](const uint16_t *p, float *f) {
+        if constexpr (CPL == 8) {
+            unpack8h(*reinterpret_cast<const uint4 *>(p + CPL * part), f);
+        } else {
+            const uint2 x = *reinterpret_cast<const uint2 *>(p + CPL * part);
+            const uint32_t w[2] = {x.x, x.y};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[i] = h2f((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
+        }
+    };
+
+    float qv[G][CPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) load_row(qu + h * D, qv[h]);
+
+    float mloc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
+    const int npass = (nt + 3) / 4;
+    for (int p0 = 0; p0 < npass; p0 += PB) {
+        float kf[PB][CPL];
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+            const int t = min((p0 + b) * 4 + ph, nt - 1);
+            load_row(row_ptr(kr, kn, t0 + t), kf[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+            const int t = (p0 + b) * 4 + ph;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) s += qv[h][i] * kf[b][i];
+                s = row16_sum(s) * a.qscale;
+                if (t < nt) {
+                    mloc[h] = fmaxf(mloc[h], s);
+                    if (part == 0) L.ls[h * kLsStride + t] = s;
+                }
+            }
+        }
+    }
+    float m_h[G], l_h[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float m = mloc[h];
+        m = fmaxf(m, shfl_xor(m, 16));
+        m = fmaxf(m, shfl_xor(m, 32));
+        m_h[h] = m;
+        l_h[h] = 0.f;
+    }
+    wave_lds_sync();
+    for (int t = lane; t < nt; t += 64)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float p = __builtin_amdgcn_exp2f(L.ls[h * kLsStride + t] - m_h[h]);
+            L.ls[h * kLsStride + t] = p;
+            l_h[h] += p;
+        }
+#pragma unroll
+    for (int h = 0; h < G; ++h) l_h[h] = wave_sum(l_h[h]);
+    wave_lds_sync();
+
+    float o[G][CPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) o[h][i] = 0.f;
+    for (int p0 = 0; p0 < npass; p0 += PB) {
+        float vf[PB][CPL];
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+            const int t = min((p0 + b) * 4 + ph, nt - 1);
+            load_row(row_ptr(vr, vn, t0 + t), vf[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+            const int t = (p0 + b) * 4 + ph;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float p = t < nt ? L.ls[h * kLsStride + min(t, nt - 1)] : 0.f;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) o[h][i] += p * vf[b][i];
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            float v = o[h][i];
+            v += shfl_xor(v, 16);
+            v += shfl_xor(v, 32);
+            o[h][i] = v;
+        }
+    wave_lds_sync();
+    if (ph == 0)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) L.ls[h * D + CPL * part + i] = o[h][i];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m_out[h] = m_h[h];
+        l_out[h] = l_h[h];
+    }
+}
+
+// FULLV: value channel groups of 16 (D/16 scales per token).
+template <int D, int G, bool FULLV>
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
     const int unit = blockIdx.y;
     const int split = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const CacheView &c = a.c;
 
-    __shared__ float p_s[kWaves][MAXW * G];   // logits, then probabilities
-    __shared__ float red_o[kWaves][G * D];
+    __shared__ WaveLds<D, G> lds[kWaves];
     __shared__ float red_ml[kWaves][G][2];
     __shared__ float mrg[G][2];
 
-    const bool resid = split >= a.n_chunks;
-    const int wchunk = a.chunk / kWaves;
-    int t0, nt;                               // this wave's tokens
-    if (!resid) {
-        t0 = split * a.chunk + wave * wchunk;
-        nt = max(0, min(wchunk, a.n_packed - t0));
+    float m_w[G], l_w[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m_w[h] = -INFINITY;
+        l_w[h] = 0.f;
+    }
+    if (split < a.n_chunks) {
+        const int wchunk = a.chunk / kWaves;
+        const int t0 = split * a.chunk + wave * wchunk;
+        const int nt = max(0, min(wchunk, a.n_packed - t0));
+        if (nt > 0) packed_wave<D, G, FULLV>(a, unit, t0, nt, lds[wave], m_w, l_w);
     } else {
         const int per = (a.n_res + kWaves - 1) / kWaves;
-        t0 = wave * per;
-        nt = max(0, min(per, a.n_res - t0));
-    }
-    const uint16_t *qu = a.q + (size_t)unit * G * D;
-    float *ps = p_s[wave];
-
-    // value-row batch of this lane: requested now, used after the softmax
-    const int vj = lane % WPT;                // channels 16 vj .. 16 vj + 15
-    const int vts = lane / WPT;
-    const int gpt = D / c.Gv;
-    const int gsel = (vj * 16) / c.Gv;
-    const uint32_t *vw = reinterpret_cast<const uint32_t *>(c.vq) +
-                         (size_t)unit * c.vq_unit() + (size_t)t0 * WPT + vj;
-    const uint16_t *vsr = c.vs + (size_t)unit * c.vm_unit() + (size_t)t0 * gpt + gsel;
-    const uint16_t *vzr = c.vz + (size_t)unit * c.vm_unit() + (size_t)t0 * gpt + gsel;
-    uint32_t vwd[VB];
-    uint16_t vsb[VB], vzb[VB];
-    auto load_vbatch = [&](int tb) {
-#pragma unroll
-        for (int i = 0; i < VB; ++i) {
-            const int t = min(tb + i * TS, nt - 1);
-            vwd[i] = vw[(size_t)t * WPT];
-            vsb[i] = vsr[(size_t)t * gpt];
-            vzb[i] = vzr[(size_t)t * gpt];
-        }
-    };
-    if (!resid && nt > 0) load_vbatch(vts);
-
-    // --------------------------------------------------------- logits
-    float m_w[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) m_w[h] = -INFINITY;
-    if (!resid) {
-        constexpr int CPL = D / 16;           // channels per lane
-        const int part = lane & 15;           // channels CPL part .. + CPL-1
-        const int rsub = lane >> 4;           // row of the 4-row pass
-        float qv[CPL][G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float f[CPL];
-            load_halves<CPL>(qu + h * D + CPL * part, f);
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) qv[i][h] = f[i] * a.qscale;
-        }
-        const uint32_t *kq = reinterpret_cast<const uint32_t *>(c.kq) +
-                             (size_t)unit * c.kq_unit();
-        const uint16_t *ks = c.ks + (size_t)unit * c.km_unit();
-        const uint16_t *kz = c.kz + (size_t)unit * c.km_unit();
-        const int nrows = nt >> 4;
-        uint32_t wds[CPL];
-        float sv[CPL], zv[CPL];
-        auto load_row = [&](int row, uint32_t *w, float *sp, float *zp) {
-            const int wrow = (t0 >> 4) + row;
-            const int grp = (wrow << 4) / c.Gk;
-            load_words<CPL>(kq + (size_t)wrow * D + CPL * part, w);
-            load_halves<CPL>(ks + (size_t)grp * D + CPL * part, sp);
-            load_halves<CPL>(kz + (size_t)grp * D + CPL * part, zp);
-        };
-        // row r0 + rsub of each 4-row pass; a row past the end re-reads the
-        // last row and its result is discarded
-        if (nrows > 0) load_row(min(rsub, nrows - 1), wds, sv, zv);
-        for (int r0 = 0; r0 < nrows; r0 += 4) {
-            const int row = r0 + rsub;
-            uint32_t nwds[CPL];
-            float nsv[CPL], nzv[CPL];
-            load_row(min(row + 4, nrows - 1), nwds, nsv, nzv);
-            if (row < nrows) {
-                float acc[16][G];
-                float bias[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    bias[h] = 0.f;
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) acc[t][h] = 0.f;
-                }
-#pragma unroll
-                for (int ch = 0; ch < CPL; ++ch) {
-                    float W[G];
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        W[h] = qv[ch][h] * sv[ch];
-                        bias[h] += qv[ch][h] * zv[ch];
-                    }
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        // bytes of m: codes of tokens k, 4+k, 8+k, 12+k
-                        const uint32_t m = (wds[ch] >> (2 * k)) & 0x03030303u;
-                        const float c0 = (float)(m & 0xff);
-                        const float c1 = (float)((m >> 8) & 0xff);
-                        const float c2 = (float)((m >> 16) & 0xff);
-                        const float c3 = (float)(m >> 24);
-#pragma unroll
-                        for (int h = 0; h < G; ++h) {
-                            acc[k][h] += W[h] * c0;
-                            acc[4 + k][h] += W[h] * c1;
-                            acc[8 + k][h] += W[h] * c2;
-                            acc[12 + k][h] += W[h] * c3;
-                        }
-                    }
-                }
-                // lane `part` keeps token `part` of the row
-                float mine[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) mine[h] = 0.f;
-#pragma unroll
-                for (int t = 0; t < 16; ++t)
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        const float v = row16_sum(acc[t][h] + bias[h]);
-                        if (t == part) mine[h] = v;
-                    }
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    ps[(row * 16 + part) * G + h] = mine[h];
-                    m_w[h] = fmaxf(m_w[h], mine[h]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                wds[i] = nwds[i];
-                sv[i] = nsv[i];
-                zv[i] = nzv[i];
-            }
-        }
-    } else {
-        // residual: one lane per token, fp16 keys; the fused new token is
-        // read from the call's input
-        const uint16_t *kr = c.kres + (size_t)unit * c.res_unit();
-        for (int t = lane; t < nt; t += 64) {
-            const int slot = t0 + t;
-            const uint16_t *krow = (a.k_new && slot == a.new_slot)
-                                       ? a.k_new + (size_t)unit * D
-                                       : kr + (size_t)slot * D;
-            float acc[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) acc[h] = 0.f;
-            const uint4 *row = reinterpret_cast<const uint4 *>(krow);
-#pragma unroll 2
-            for (int i = 0; i < D / 8; ++i) {
-                float kf[8];
-                unpack8h(row[i], kf);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    float qf[8];
-                    unpack8h(*reinterpret_cast<const uint4 *>(qu + h * D + 8 * i), qf);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) acc[h] += qf[j] * kf[j];
-                }
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float v = acc[h] * a.qscale;
-                ps[t * G + h] = v;
-                m_w[h] = fmaxf(m_w[h], v);
-            }
-        }
+        const int t0 = wave * per;
+        const int nt = max(0, min(per, a.n_res - t0));
+        if (nt > 0) residual_wave<D, G>(a, unit, t0, nt, lds[wave], m_w, l_w);
         // store the new token into its residual slot for later calls
         if (a.k_new && wave == 0 && lane < 2 * (D / 8)) {
             const int part = lane % (D / 8);
@@ -300,131 +665,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
                             (size_t)a.new_slot * D;
             reinterpret_cast<uint4 *>(dst)[part] = reinterpret_cast<const uint4 *>(src)[part];
         }
-    }
-
-    // ------------------------------------------------ wave softmax stats
-    float l_w[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) m_w[h] = wave_max(m_w[h]);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-#pragma unroll
-    for (int h = 0; h < G; ++h) l_w[h] = 0.f;
-    for (int t = lane; t < nt; t += 64)
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float p = __builtin_amdgcn_exp2f(ps[t * G + h] - m_w[h]);
-            ps[t * G + h] = p;
-            l_w[h] += p;
-        }
-#pragma unroll
-    for (int h = 0; h < G; ++h) l_w[h] = wave_sum(l_w[h]);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-
-    // ----------------------------------------------------------- P . V
-    if (!resid) {
-        float acc[G][16];
-        float zs[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            zs[h] = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
-        }
-        for (int tb = vts; tb < nt; tb += VB * TS) {
-            uint32_t cwd[VB];
-            uint16_t csb[VB], czb[VB];
-#pragma unroll
-            for (int i = 0; i < VB; ++i) {
-                cwd[i] = vwd[i];
-                csb[i] = vsb[i];
-                czb[i] = vzb[i];
-            }
-            load_vbatch(tb + VB * TS);            // next batch (clamped)
-#pragma unroll
-            for (int i = 0; i < VB; ++i) {
-                const int t = tb + i * TS;
-                const bool ok = t < nt;
-                const int tc = min(t, nt - 1);
-                const float s = h2f(csb[i]);
-                const float z = h2f(czb[i]);
-                float pss[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float p = ok ? ps[tc * G + h] : 0.f;
-                    pss[h] = p * s;
-                    zs[h] += p * z;
-                }
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    // bytes of m: codes of channels k, 4+k, 8+k, 12+k
-                    const uint32_t m = (cwd[i] >> (2 * k)) & 0x03030303u;
-                    const float c0 = (float)(m & 0xff);
-                    const float c1 = (float)((m >> 8) & 0xff);
-                    const float c2 = (float)((m >> 16) & 0xff);
-                    const float c3 = (float)(m >> 24);
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        acc[h][k] += pss[h] * c0;
-                        acc[h][4 + k] += pss[h] * c1;
-                        acc[h][8 + k] += pss[h] * c2;
-                        acc[h][12 + k] += pss[h] * c3;
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float v = acc[h][e] + zs[h];
-                for (int off = WPT; off < 64; off <<= 1) v += shfl_xor(v, off);
-                acc[h][e] = v;
-            }
-        if (lane < WPT)
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) red_o[wave][h * D + vj * 16 + e] = acc[h][e];
-    } else {
-        constexpr int CPT = D / 8;            // uint4 per residual row
-        constexpr int RTS = 64 / CPT;
-        const int c8 = lane % CPT;
-        const int ts = lane / CPT;
-        const uint16_t *vr = c.vres + (size_t)unit * c.res_unit();
-        float acc[G][8];
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-        for (int t = ts; t < nt; t += RTS) {
-            const int slot = t0 + t;
-            const uint16_t *vrow = (a.v_new && slot == a.new_slot)
-                                       ? a.v_new + (size_t)unit * D
-                                       : vr + (size_t)slot * D;
-            float vf[8];
-            unpack8h(reinterpret_cast<const uint4 *>(vrow)[c8], vf);
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float p = ps[t * G + h];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] += p * vf[e];
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float v = acc[h][e];
-                for (int off = CPT; off < 64; off <<= 1) v += shfl_xor(v, off);
-                acc[h][e] = v;
-            }
-        if (lane < CPT)
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) red_o[wave][h * D + c8 * 8 + e] = acc[h][e];
     }
     if (lane == 0)
 #pragma unroll
@@ -437,7 +677,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
     // ----------------------------------------- merge the 4 waves, store
     if (tid < G) {
         float M = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][tid][0]);
+        for (int w = 0; w < kWaves; ++w)
+            if (red_ml[w][tid][1] > 0.f) M = fmaxf(M, red_ml[w][tid][0]);
         float L = 0.f;
         for (int w = 0; w < kWaves; ++w)
             if (red_ml[w][tid][1] > 0.f)
@@ -453,7 +694,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecArgs a) {
         float v = 0.f;
         for (int w = 0; w < kWaves; ++w)
             if (red_ml[w][h][1] > 0.f)
-                v += red_o[w][i] * __builtin_amdgcn_exp2f(red_ml[w][h][0] - M);
+                v += lds[w].ls[i] * __builtin_amdgcn_exp2f(red_ml[w][h][0] - M);
         a.part_o[sbase * G * D + i] = v;
     }
     if (tid < G) {
@@ -529,26 +770,27 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     }
 }
 
-int max_wave_chunk(int g) {
-    return kMaxWaveChunk * g <= 1024 ? kMaxWaveChunk : 1024 / g;
-}
-
 // Largest chunk that still gives ~4 blocks per CU, never more than
-// kMaxSplit - 1 packed splits per unit.
-int pick_chunk(int units, int n_packed, int g) {
-    const int maxw = max_wave_chunk(g);
-    for (int w = maxw; w > kMinWaveChunk; w >>= 1) {
+// kMaxSplit - 1 packed splits per unit.  A wave's share is a power of two
+// between max(kMinWaveChunk, Gk) and kMaxWaveChunk tokens, so it holds whole
+// key groups and whole 32-token value steps.
+int pick_chunk(int units, int n_packed, int Gk) {
+    const int minw = std::max(kMinWaveChunk, Gk);
+    for (int w = kMaxWaveChunk; w > minw; w >>= 1) {
         const int ch = w * kWaves;
         const int next = ch / 2;
         if ((long)units * ((n_packed + ch - 1) / ch) >= 1024) return ch;
         if ((n_packed + next - 1) / next > kMaxSplit - 1) return ch;
     }
-    return kMinWaveChunk * kWaves;
+    return minw * kWaves;
 }
 
 template <int D, int G>
 hipError_t launch_decode_dg(const DecArgs &a, int units, hipStream_t stream) {
-    decode_kernel<D, G><<<dim3(a.nsplit, units), kThreads, 0, stream>>>(a);
+    if (a.c.Gv == 16)
+        decode_kernel<D, G, true><<<dim3(a.nsplit, units), kThreads, 0, stream>>>(a);
+    else
+        decode_kernel<D, G, false><<<dim3(a.nsplit, units), kThreads, 0, stream>>>(a);
     decode_combine_kernel<D, G><<<dim3(G, units), kThreads, 0, stream>>>(
         a.part_ml, a.part_o, a.nsplit, a.o);
     return hipGetLastError();
@@ -578,7 +820,8 @@ size_t decode_ws_bytes(int units, int g, int D, int capacity) {
 }
 
 int decode_max_capacity(int g) {
-    return (kMaxSplit - 1) * max_wave_chunk(g) * kWaves;
+    (void)g;
+    return (kMaxSplit - 1) * kMaxWaveChunk * kWaves;
 }
 
 hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
@@ -591,7 +834,7 @@ hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
     a.c = c;
     a.n_packed = n_packed;
     a.n_res = n_res;
-    a.chunk = pick_chunk(units, n_packed, g);
+    a.chunk = pick_chunk(units, n_packed, c.Gk);
     a.n_chunks = (n_packed + a.chunk - 1) / a.chunk;
     a.nsplit = a.n_chunks + (n_res > 0 ? 1 : 0);
     a.qscale = kLog2e / sqrtf((float)c.D);

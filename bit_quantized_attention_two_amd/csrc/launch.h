@@ -17,9 +17,9 @@ struct CacheView {
     uint16_t *vs, *vz;
     uint16_t *kres, *vres;
     int cap, nr, D, Gk, Gv;
-    __host__ __device__ size_t kq_unit() const { return (size_t)(cap / 16) * D; }
+    __host__ __device__ size_t kq_unit() const { return (size_t)cap * (D / 16); }
     __host__ __device__ size_t km_unit() const { return (size_t)(cap / Gk) * D; }
-    __host__ __device__ size_t vq_unit() const { return (size_t)cap * (D / 16); }
+    __host__ __device__ size_t vq_unit() const { return (size_t)(cap / 16) * D; }
     __host__ __device__ size_t vm_unit() const { return (size_t)cap * (D / Gv); }
     __host__ __device__ size_t res_unit() const { return (size_t)nr * D; }
 };

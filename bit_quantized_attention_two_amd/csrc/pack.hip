@@ -47,56 +47,90 @@ __device__ __forceinline__ uint32_t code_of(float x, const QParams &p) {
            (uint32_t)(d > p.t2);
 }
 
-// Keys: one thread per (key group, channel).  The group's Gk source rows are
-// read twice (min/max, then codes); both reads are coalesced across the
-// channel-contiguous threads and the second hits the cache.
+// OR of a value over the 16 lanes of a DPP row; every lane gets the result.
+__device__ __forceinline__ uint32_t row16_or(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false);
+    return v;
+}
+
+__device__ __forceinline__ void unpack8(uint4 x, float *f) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = h2f((uint16_t)(w[j >> 1] >> (16 * (j & 1))));
+}
+
+// Keys: one thread per (key group, 8 channels), 16-byte loads of each of the
+// group's Gk source rows (read twice: min/max, then codes; the second read
+// hits the cache).  A key word holds 16 channels of one token, so the two
+// threads of a 16-channel block combine their halves of each word.
 template <int D>
 __global__ __launch_bounds__(256) void pack_keys_kernel(
     PackSrc src, int n_groups, int dst_group_off, CacheView c) {
-    constexpr int GPB = 256 / D;                 // groups per block
+    constexpr int TPG = D / 8;                   // threads per group
+    constexpr int GPB = 256 / TPG;               // groups per block
     const int unit = blockIdx.y;
-    const int gi = blockIdx.x * GPB + threadIdx.x / D;
-    const int ch = threadIdx.x % D;
-    if (gi >= n_groups) return;
+    const int gi = blockIdx.x * GPB + threadIdx.x / TPG;
+    const int oct = threadIdx.x % TPG;           // channels 8 oct .. 8 oct + 7
+    if (gi >= n_groups) return;                  // whole channel blocks leave
     const int Gk = c.Gk;
-    const uint16_t *base = src.k + (size_t)unit * src.src_unit + ch;
+    const uint16_t *base = src.k + (size_t)unit * src.src_unit + oct * 8;
     const int32_t *sel = src.sel ? src.sel + (size_t)unit * src.sel_unit
                                  : nullptr;
     const int p0 = gi * Gk;
 
-    float mn = 0.f, mx = 0.f;
+    float mn[8], mx[8];
     for (int t = 0; t < Gk; ++t) {
         const int row = sel ? sel[p0 + t] : p0 + t;
-        const float x = h2f(base[(size_t)row * D]);
-        if (t == 0) {
-            mn = x;
-            mx = x;
-        } else {
-            if (x < mn) mn = x;
-            if (x > mx) mx = x;
+        float x[8];
+        unpack8(*reinterpret_cast<const uint4 *>(base + (size_t)row * D), x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (t == 0) {
+                mn[j] = x[j];
+                mx[j] = x[j];
+            } else {
+                if (x[j] < mn[j]) mn[j] = x[j];
+                if (x[j] > mx[j]) mx[j] = x[j];
+            }
         }
     }
-    const QParams qp = qparams(mn, mx);
+    QParams qp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qp[j] = qparams(mn[j], mx[j]);
 
     const int g_out = dst_group_off + gi;
     int32_t *kq = c.kq + (size_t)unit * c.kq_unit() +
-                  (size_t)(g_out * Gk / 16) * D + ch;
-    for (int w = 0; w < Gk / 16; ++w) {
-        uint32_t word = 0;
-        for (int e = 0; e < 16; ++e) {
-            const int p = p0 + w * 16 + e;
-            const int row = sel ? sel[p] : p;
-            word |= code_of(h2f(base[(size_t)row * D]), qp) << (2 * e);
-        }
-        kq[(size_t)w * D] = (int32_t)word;
+                  (size_t)g_out * Gk * (D / 16) + oct / 2;
+    const int sh = 16 * (oct & 1);               // this thread's half-word
+    for (int t = 0; t < Gk; ++t) {
+        const int row = sel ? sel[p0 + t] : p0 + t;
+        float x[8];
+        unpack8(*reinterpret_cast<const uint4 *>(base + (size_t)row * D), x);
+        uint32_t half = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) half |= code_of(x[j], qp[j]) << (sh + 2 * j);
+        const uint32_t word = half | (uint32_t)__shfl_xor((int)half, 1);
+        if ((oct & 1) == 0) kq[(size_t)t * (D / 16)] = (int32_t)word;
     }
-    const size_t mo = (size_t)unit * c.km_unit() + (size_t)g_out * D + ch;
-    c.ks[mo] = qp.sh;
-    c.kz[mo] = qp.zh;
+    const size_t mo = (size_t)unit * c.km_unit() + (size_t)g_out * D + oct * 8;
+    uint32_t sw[4], zw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        sw[j] = (uint32_t)qp[2 * j].sh | ((uint32_t)qp[2 * j + 1].sh << 16);
+        zw[j] = (uint32_t)qp[2 * j].zh | ((uint32_t)qp[2 * j + 1].zh << 16);
+    }
+    *reinterpret_cast<uint4 *>(c.ks + mo) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+    *reinterpret_cast<uint4 *>(c.kz + mo) = make_uint4(zw[0], zw[1], zw[2], zw[3]);
 }
 
 // Values: one thread per (token, channel group); the group's Gv halves are
-// read with 16-byte loads.
+// read with 16-byte loads.  A value word holds 16 tokens of one channel: the
+// 16 lanes of a DPP row take 16 consecutive tokens of the same channel group
+// and OR their codes together, lane e keeping the words of channels
+// 16 j + e of the group.  Token counts are multiples of 16.
 template <int D>
 __global__ __launch_bounds__(256) void pack_values_kernel(
     PackSrc src, int n_tok, int dst_off, CacheView c) {
@@ -104,25 +138,27 @@ __global__ __launch_bounds__(256) void pack_values_kernel(
     const int Gv = c.Gv;
     const int gpt = D / Gv;                      // groups per token
     const int idx = blockIdx.x * 256 + threadIdx.x;
-    const int p = idx / gpt;
-    const int G = idx % gpt;
-    if (p >= n_tok) return;
+    const int e = idx & 15;                      // token within its block
+    const int bg = idx >> 4;
+    const int blk = bg / gpt;                    // 16-token block
+    const int G = bg % gpt;
+    const int p = blk * 16 + e;
+    if (p >= n_tok) return;                      // whole rows leave
     const int row = src.sel ? src.sel[(size_t)unit * src.sel_unit + p] : p;
     const uint4 *x4 = reinterpret_cast<const uint4 *>(
         src.v + (size_t)unit * src.src_unit + (size_t)row * D + G * Gv);
 
     float mn = 0.f, mx = 0.f;
     for (int i = 0; i < Gv / 8; ++i) {
-        const uint4 q = x4[i];
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        float x[8];
+        unpack8(x4[i], x);
         for (int j = 0; j < 8; ++j) {
-            const float x = h2f((uint16_t)(w[j / 2] >> (16 * (j & 1))));
             if (i == 0 && j == 0) {
-                mn = x;
-                mx = x;
+                mn = x[j];
+                mx = x[j];
             } else {
-                if (x < mn) mn = x;
-                if (x > mx) mx = x;
+                if (x[j] < mn) mn = x[j];
+                if (x[j] > mx) mx = x[j];
             }
         }
     }
@@ -130,18 +166,19 @@ __global__ __launch_bounds__(256) void pack_values_kernel(
 
     const int t_out = dst_off + p;
     int32_t *vq = c.vq + (size_t)unit * c.vq_unit() +
-                  (size_t)t_out * (D / 16) + G * Gv / 16;
+                  (size_t)(t_out >> 4) * D + G * Gv + e;
     for (int wi = 0; wi < Gv / 16; ++wi) {
-        uint32_t word = 0;
-        for (int h = 0; h < 2; ++h) {
-            const uint4 q = x4[wi * 2 + h];
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        uint32_t mine = 0;
+        for (int hh = 0; hh < 2; ++hh) {
+            float x[8];
+            unpack8(x4[wi * 2 + hh], x);
+#pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float x = h2f((uint16_t)(w[j / 2] >> (16 * (j & 1))));
-                word |= code_of(x, qp) << (2 * (h * 8 + j));
+                const uint32_t w = row16_or(code_of(x[j], qp) << (2 * e));
+                if (hh * 8 + j == e) mine = w;
             }
         }
-        vq[wi] = (int32_t)word;
+        vq[wi * 16] = (int32_t)mine;
     }
     const size_t mo = (size_t)unit * c.vm_unit() + (size_t)t_out * gpt + G;
     c.vs[mo] = qp.sh;
@@ -188,9 +225,9 @@ hipError_t launch_pack(const PackSrc &src, int units, int n_tok, int n_tail,
                        int dst_off, const CacheView &c, hipStream_t stream) {
     if (n_tok > 0) {
         const int n_groups = n_tok / c.Gk;
-        const int gpb = 256 / c.D;
+        const int gpb = 256 / (c.D / 8);
         dim3 gk((n_groups + gpb - 1) / gpb, units);
-        const int vthreads = n_tok * (c.D / c.Gv);
+        const int vthreads = n_tok * (c.D / c.Gv);   // n_tok % 16 == 0
         dim3 gv((vthreads + 255) / 256, units);
         if (c.D == 128) {
             pack_keys_kernel<128><<<gk, 256, 0, stream>>>(

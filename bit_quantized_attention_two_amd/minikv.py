@@ -189,10 +189,10 @@ class LayerCache:
         U, D = dims.units, dims.head_dim
         Gk, Gv, nr = dims.group_k, dims.group_v, dims.residual_cap
         shapes = {
-            "kq": ((U, capacity // 16, D), torch.int32),
+            "kq": ((U, capacity, D // 16), torch.int32),
             "k_scale": ((U, capacity // Gk, D), torch.float16),
             "k_zero": ((U, capacity // Gk, D), torch.float16),
-            "vq": ((U, capacity, D // 16), torch.int32),
+            "vq": ((U, capacity // 16, D), torch.int32),
             "v_scale": ((U, capacity, D // Gv), torch.float16),
             "v_zero": ((U, capacity, D // Gv), torch.float16),
             "k_res": ((U, nr, D), torch.float16),

@@ -75,14 +75,16 @@ typedef struct minikv_dims {
 
 /* One layer's compressed cache.  Device arrays (sizes from
  * minikv_cache_layout), cap = capacity:
- *   kq      int32  [B][Hkv][cap/16][D]   word (w, c) holds the 2-bit codes of
- *                                        packed tokens 16w..16w+15 of channel
- *                                        c; token 16w+e at bits 2e..2e+1
- *   k_scale fp16   [B][Hkv][cap/Gk][D]   per key group and channel
- *   k_zero  fp16   [B][Hkv][cap/Gk][D]
- *   vq      int32  [B][Hkv][cap][D/16]   word (t, j) holds the codes of
+ *   kq      int32  [B][Hkv][cap][D/16]   word (t, j) holds the 2-bit codes of
  *                                        channels 16j..16j+15 of packed token
  *                                        t; channel 16j+e at bits 2e..2e+1
+ *   k_scale fp16   [B][Hkv][cap/Gk][D]   per key group and channel
+ *   k_zero  fp16   [B][Hkv][cap/Gk][D]
+ *   vq      int32  [B][Hkv][cap/16][D]   word (w, c) holds the codes of
+ *                                        packed tokens 16w..16w+15 of channel
+ *                                        c; token 16w+e at bits 2e..2e+1
+ *           (each word runs along the dimension attention sums over:
+ *           channels for q.k, tokens for p.v)
  *   v_scale fp16   [B][Hkv][cap][D/Gv]   per token and channel group
  *   v_zero  fp16   [B][Hkv][cap][D/Gv]
  *   k_res   fp16   [B][Hkv][nr][D]       residual keys, slots 0..n_res-1
@@ -228,8 +230,7 @@ MINIKV_API int32_t minikv_append(const minikv_dims *dims, minikv_layer_cache *ca
  *   the split partial results; calls that share a workspace must not overlap
  *   in time.
  * EINVAL if the cache holds no token; EUNSUPPORTED if capacity exceeds
- * 511 * 2048 packed tokens (g <= 2; 511 * 1024 for g = 4, 511 * 512 for
- * g = 8). */
+ * 511 * 1024 packed tokens. */
 MINIKV_API int32_t minikv_decode_attn(const minikv_dims *dims,
                            const minikv_layer_cache *cache, const void *q,
                            void *o, void *ws, size_t ws_bytes, void *stream);

@@ -64,8 +64,8 @@ def assert_cache_equal(gpu_cache, ocache, B, Hkv):
     g = cache_to_numpy(gpu_cache)
     npk, nres = ocache.n_packed, ocache.n_res
     Gk = ocache.Gk
-    sl = {"kq": np.s_[:, :, :npk // 16], "k_scale": np.s_[:, :, :npk // Gk],
-          "k_zero": np.s_[:, :, :npk // Gk], "vq": np.s_[:, :, :npk],
+    sl = {"kq": np.s_[:, :, :npk], "k_scale": np.s_[:, :, :npk // Gk],
+          "k_zero": np.s_[:, :, :npk // Gk], "vq": np.s_[:, :, :npk // 16],
           "v_scale": np.s_[:, :, :npk], "v_zero": np.s_[:, :, :npk],
           "k_res": np.s_[:, :, :nres], "v_res": np.s_[:, :, :nres]}
     for name, oname in ORACLE_NAMES.items():
