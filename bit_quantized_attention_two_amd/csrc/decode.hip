@@ -104,10 +104,15 @@ __device__ __forceinline__ half8_t code_operand(uint32_t x) {
     return __builtin_bit_cast(half8_t, v);
 }
 
-// fp16 hi + lo of a weight (hi rounded to nearest, lo the rounded rest).
-__device__ __forceinline__ void split2(float w, half_t &hi, half_t &lo) {
-    hi = (half_t)w;
-    lo = (half_t)(w - (float)hi);
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+// fp16 hi + lo of two weights: hi truncated (one v_cvt_pkrtz for both), lo
+// the rest w - hi, exact in fp32, rounded to fp16.  hi + lo holds w to
+// about 22 bits.
+__device__ __forceinline__ void split2x2(float w0, float w1, uint32_t &hi, uint32_t &lo) {
+    const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(w0, w1));
+    const half2_t l = {(half_t)(w0 - (float)h[0]), (half_t)(w1 - (float)h[1])};
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
 }
 
 __device__ __forceinline__ void unpack8h(uint4 x, float *f) {
@@ -241,7 +246,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
 #pragma unroll
         for (int j = 0; j < TPB; ++j) {
             const int t = min(tok + 16 * j + r, nt - 1);
-            const uint32_t *wp = kq + (size_t)(t0 + t) * KW + (qd >> 1) * KB;
+            const uint32_t *wp = kq + (uint32_t)((t0 + t) * KW + (qd >> 1) * KB);
             if constexpr (KB == 4) {
                 const uint4 x = *reinterpret_cast<const uint4 *>(wp);
                 kw[j][0] = x.x; kw[j][1] = x.y; kw[j][2] = x.z; kw[j][3] = x.w;
@@ -259,17 +264,23 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         for (int kb = 0; kb < KB; ++kb) {
             const uint32_t sx[2][2] = {{ksr[kb][0].x, ksr[kb][0].y},
                                        {ksr[kb][1].x, ksr[kb][1].y}};
+            u32x4 hw, lw;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                float w[2];
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     const float sc = h2f((uint16_t)(sx[hf][i >> 1] >> (16 * (i & 1))));
                     const float qv = h2f((uint16_t)(qh[kb][i] >> (16 * hf)));
-                    half_t h_, l_;
-                    split2(__builtin_amdgcn_ldexpf(qv * sc, -qe - 2 * i), h_, l_);
-                    bhi[kb][2 * i + hf] = h_;
-                    blo[kb][2 * i + hf] = l_;
+                    w[hf] = __builtin_amdgcn_ldexpf(qv * sc, -qe - 2 * i);
                 }
+                uint32_t h_, l_;
+                split2x2(w[0], w[1], h_, l_);
+                hw[i] = h_;
+                lw[i] = l_;
+            }
+            bhi[kb] = __builtin_bit_cast(half8_t, hw);
+            blo[kb] = __builtin_bit_cast(half8_t, lw);
         }
     };
     // z terms of the operand's groups (rows) for every head (columns), in
@@ -413,7 +424,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         uint32_t vw[MBP];
         auto load_vw = [&](int st) {
             const int blk = min((t0 + st) / 16 + (qd >> 1), last_blk);
-            const uint32_t *wp = vq + (size_t)blk * D + P * CP + r * MBP;
+            const uint32_t *wp = vq + (uint32_t)(blk * D + P * CP + r * MBP);
             if constexpr (MBP == 8) {
                 const uint4 x0 = *reinterpret_cast<const uint4 *>(wp);
                 const uint4 x1 = *reinterpret_cast<const uint4 *>(wp + 4);
@@ -446,17 +457,19 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             const half4_t s1 = *reinterpret_cast<const half4_t *>(sp + 8);
             const half4_t z0 = *reinterpret_cast<const half4_t *>(zp);
             const half4_t z1 = *reinterpret_cast<const half4_t *>(zp + 8);
-            half8_t bh, bl;
+            u32x4 bhw, blw;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                half_t h0, l0, h1, l1;
-                split2(p0[i] * (float)s0[i], h0, l0);
-                split2(p1[i] * (float)s1[i], h1, l1);
-                bh[2 * i] = h0; bh[2 * i + 1] = h1;
-                bl[2 * i] = l0; bl[2 * i + 1] = l1;
+                uint32_t hw, lw;
+                split2x2(p0[i] * (float)s0[i], p1[i] * (float)s1[i], hw, lw);
+                bhw[i] = hw;
+                blw[i] = lw;
                 // p is stored times 4^-i: keep one z sum per i
-                za[i] += p0[i] * (float)z0[i] + p1[i] * (float)z1[i];
+                za[i] = __builtin_fmaf(p0[i], (float)z0[i], za[i]);
+                za[i] = __builtin_fmaf(p1[i], (float)z1[i], za[i]);
             }
+            const half8_t bh = __builtin_bit_cast(half8_t, bhw);
+            const half8_t bl = __builtin_bit_cast(half8_t, blw);
 #pragma unroll
             for (int mb = 0; mb < MBP; ++mb) {
                 acc[mb] = mfma16(av[mb], bh, acc[mb]);
