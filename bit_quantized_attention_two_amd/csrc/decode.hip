@@ -110,7 +110,9 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // about 22 bits.
 __device__ __forceinline__ void split2x2(float w0, float w1, uint32_t &hi, uint32_t &lo) {
     const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(w0, w1));
-    const half2_t l = {(half_t)(w0 - (float)h[0]), (half_t)(w1 - (float)h[1])};
+    // w - hi in one mixed-precision FMA each (v_fma_mix{lo,hi}_f16)
+    const half2_t l = {(half_t)__builtin_fmaf((float)h[0], -1.f, w0),
+                       (half_t)__builtin_fmaf((float)h[1], -1.f, w1)};
     hi = __builtin_bit_cast(uint32_t, h);
     lo = __builtin_bit_cast(uint32_t, l);
 }
@@ -216,6 +218,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     // logit (log2 units) = (acc * 2^(24 + e) + z term) * qscale
     const float kfac = __builtin_amdgcn_ldexpf(a.qscale, 24 + qe);
 
+
     // ---- loaders (indices clamped, never predicated)
     uint2 ksr[KB][2];                             // key scales of a B operand
     auto load_kscale = [&](int tok) {             // B operand holding tok
@@ -270,9 +273,10 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                 float w[2];
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
-                    const float sc = h2f((uint16_t)(sx[hf][i >> 1] >> (16 * (i & 1))));
-                    const float qv = h2f((uint16_t)(qh[kb][i] >> (16 * hf)));
-                    w[hf] = __builtin_amdgcn_ldexpf(qv * sc, -qe - 2 * i);
+                    const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(sx[hf][i >> 1] >> (16 * (i & 1))));
+                    const half_t qv = __builtin_bit_cast(half_t, (uint16_t)(qh[kb][i] >> (16 * hf)));
+                    // exact fp16 x fp16 product (v_fma_mix_f32), then 2^-e 4^-i
+                    w[hf] = __builtin_amdgcn_ldexpf(__builtin_fmaf((float)qv, (float)sc, 0.f), -qe - 2 * i);
                 }
                 uint32_t h_, l_;
                 split2x2(w[0], w[1], h_, l_);
@@ -461,7 +465,8 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t hw, lw;
-                split2x2(p0[i] * (float)s0[i], p1[i] * (float)s1[i], hw, lw);
+                split2x2(__builtin_fmaf(p0[i], (float)s0[i], 0.f),
+                         __builtin_fmaf(p1[i], (float)s1[i], 0.f), hw, lw);
                 bhw[i] = hw;
                 blw[i] = lw;
                 // p is stored times 4^-i: keep one z sum per i
@@ -641,7 +646,7 @@ __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0
 
 // FULLV: value channel groups of 16 (D/16 scales per token).
 template <int D, int G, bool FULLV>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_kernel(DecArgs a) {
     const int unit = blockIdx.y;
     const int split = blockIdx.x;
     const int tid = threadIdx.x;
@@ -783,16 +788,20 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     }
 }
 
-// Largest chunk that still gives ~4 blocks per CU, never more than
-// kMaxSplit - 1 packed splits per unit.  A wave's share is a power of two
-// between max(kMinWaveChunk, Gk) and kMaxWaveChunk tokens, so it holds whole
-// key groups and whole 32-token value steps.
-int pick_chunk(int units, int n_packed, int Gk) {
+// Largest chunk whose blocks still fill half of the resident block slots
+// (blocks per CU from the kernels' register and LDS use: 4 for g = 1, 3
+// for g = 4, 2 for g = 2 and 8), never more than kMaxSplit - 1 packed
+// splits per unit.  A wave's share is a power of two between
+// max(kMinWaveChunk, Gk) and kMaxWaveChunk tokens, so it holds whole key
+// groups and whole 32-token value steps.
+int pick_chunk(int units, int n_packed, int Gk, int g) {
+    const int per_cu = g == 1 ? 4 : g == 4 ? 3 : 2;
+    const long want = 256L * per_cu / 2;
     const int minw = std::max(kMinWaveChunk, Gk);
     for (int w = kMaxWaveChunk; w > minw; w >>= 1) {
         const int ch = w * kWaves;
         const int next = ch / 2;
-        if ((long)units * ((n_packed + ch - 1) / ch) >= 1024) return ch;
+        if ((long)units * ((n_packed + ch - 1) / ch) >= want) return ch;
         if ((n_packed + next - 1) / next > kMaxSplit - 1) return ch;
     }
     return minw * kWaves;
@@ -847,7 +856,7 @@ hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
     a.c = c;
     a.n_packed = n_packed;
     a.n_res = n_res;
-    a.chunk = pick_chunk(units, n_packed, c.Gk);
+    a.chunk = pick_chunk(units, n_packed, c.Gk, g);
     a.n_chunks = (n_packed + a.chunk - 1) / a.chunk;
     a.nsplit = a.n_chunks + (n_res > 0 ? 1 : 0);
     a.qscale = kLog2e / sqrtf((float)c.D);
