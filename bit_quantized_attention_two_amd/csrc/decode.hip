@@ -369,29 +369,42 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     }
     wave_lds_sync();
     const int nt32 = (nt + 31) & ~31;
-    for (int t = lane; t < nt32; t += 64) {
-        const bool ok = t < nt;
-        const size_t row = (size_t)(t0 + min(t, nt - 1)) * NGV;
-        half_t sg[NG16], zg[NG16];
-        if constexpr (FULLV && NG16 == 8) {
-            const half8_t s8 = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4 *>(vs + row));
-            const half8_t z8 = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4 *>(vz + row));
+    // the value meta of all of this lane's tokens (t = lane + 64 k), loads
+    // issued together so that their latencies overlap
+    constexpr int NK = kMaxWaveChunk / 64;
+    constexpr int MW = NG16 / 2;                  // dwords of fp16 per token
+    uint32_t msr[NK][MW], mzr[NK][MW];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) { sg[j] = s8[j]; zg[j] = z8[j]; }
+    for (int k = 0; k < NK; ++k) {
+        const size_t row = (size_t)(t0 + min(lane + 64 * k, nt - 1)) * NGV;
+        if constexpr (FULLV && MW == 4) {
+            const uint4 xs = *reinterpret_cast<const uint4 *>(vs + row);
+            const uint4 xz = *reinterpret_cast<const uint4 *>(vz + row);
+            msr[k][0] = xs.x; msr[k][1] = xs.y; msr[k][2] = xs.z; msr[k][3] = xs.w;
+            mzr[k][0] = xz.x; mzr[k][1] = xz.y; mzr[k][2] = xz.z; mzr[k][3] = xz.w;
         } else if constexpr (FULLV) {
-            const half4_t s4 = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(vs + row));
-            const half4_t z4 = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(vz + row));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { sg[j] = s4[j]; zg[j] = z4[j]; }
+            const uint2 xs = *reinterpret_cast<const uint2 *>(vs + row);
+            const uint2 xz = *reinterpret_cast<const uint2 *>(vz + row);
+            msr[k][0] = xs.x; msr[k][1] = xs.y;
+            mzr[k][0] = xz.x; mzr[k][1] = xz.y;
         } else {
             // value groups of Gv > 16 channels: repeat per 16-channel part
             const int per = NG16 / NGV;
 #pragma unroll
-            for (int j = 0; j < NG16; ++j) {
-                sg[j] = __builtin_bit_cast(half_t, vs[row + j / per]);
-                zg[j] = __builtin_bit_cast(half_t, vz[row + j / per]);
+            for (int j = 0; j < MW; ++j) {
+                msr[k][j] = (uint32_t)vs[row + (2 * j) / per] |
+                            ((uint32_t)vs[row + (2 * j + 1) / per] << 16);
+                mzr[k][j] = (uint32_t)vz[row + (2 * j) / per] |
+                            ((uint32_t)vz[row + (2 * j + 1) / per] << 16);
             }
         }
+    }
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        const int t = lane + 64 * k;
+        if (64 * k >= nt32) break;                // uniform
+        if (t >= nt32) continue;
+        const bool ok = t < nt;
         const float q4 = __builtin_amdgcn_ldexpf(1.f, -2 * (t & 3));
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -400,9 +413,12 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             L.ls[h * kLsStride + t] = p * q4;
         }
 #pragma unroll
-        for (int j = 0; j < NG16; ++j) {
-            L.sv[j * kSvStride + t] = ok ? sg[j] : (half_t)0.f;
-            L.zv[j * kSvStride + t] = ok ? zg[j] : (half_t)0.f;
+        for (int j = 0; j < MW; ++j) {
+            const uint32_t sw = ok ? msr[k][j] : 0u, zw = ok ? mzr[k][j] : 0u;
+            L.sv[(2 * j) * kSvStride + t] = __builtin_bit_cast(half_t, (uint16_t)(sw & 0xffffu));
+            L.sv[(2 * j + 1) * kSvStride + t] = __builtin_bit_cast(half_t, (uint16_t)(sw >> 16));
+            L.zv[(2 * j) * kSvStride + t] = __builtin_bit_cast(half_t, (uint16_t)(zw & 0xffffu));
+            L.zv[(2 * j + 1) * kSvStride + t] = __builtin_bit_cast(half_t, (uint16_t)(zw >> 16));
         }
     }
 #pragma unroll
