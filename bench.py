@@ -55,7 +55,80 @@ def parse():
                         "the captured HIP graphs of a step")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="rough CPU budget of the oracle baseline")
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="run only the short workload whose HBM counters "
+                        "(rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) give the "
+                        "roofline's traffic: a 256 MiB device copy for "
+                        "calibration, then one decode call per layer at the "
+                        "end-of-step cache state")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama2_7b_4k_traffic.md")
+DECODE_SRC = os.path.join(ROOT, "bit_quantized_attention_two_amd", "csrc",
+                          "decode.hip")
+
+
+def measured_traffic(config_id):
+    """HBM bytes per decode call from the committed counter summary, or None
+    when it does not cover this workload or the decode source has changed
+    since the counters were taken."""
+    import hashlib
+    if config_id != 2 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith(("|", "#", " ")):
+            k, _, v = line.partition(":")
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if fields.get("decode_source_sha256") != h:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_probe():
+    """Workload for the traffic counters (see --traffic-probe)."""
+    import torch
+    from bit_quantized_attention_two_amd import configs, minikv
+    c = configs.get(2)
+    B, Hq, Hkv, D, n, L = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"], c["L"]
+    ks, r = minikv.pyramid_budgets(n, L, c["hh"], c["rw"], c["depth"],
+                                   c["pyramid"])
+    dims = minikv.make_dims(B, Hq, Hkv, D, c["Gk"], c["Gv"], c["residual_cap"])
+    torch.manual_seed(0)
+    src = torch.randn(64 * 1024 * 1024, device="cuda")      # 256 MiB
+    dst = torch.empty_like(src)
+    k = torch.randn(B, Hkv, n, D, device="cuda").half()
+    v = torch.randn(B, Hkv, n, D, device="cuda").half()
+    kn = torch.randn(B, Hkv, D, device="cuda").half()
+    caches = []
+    for l in range(L):
+        m = ks[l] + r
+        sel = (torch.arange(m, device="cuda", dtype=torch.int64) * n // m
+               ).int().repeat(B, Hkv, 1).contiguous()
+        cache = minikv.LayerCache(dims, (m // 16) * 16 + 256)
+        minikv.pack(dims, k, v, sel, cache)
+        for _ in range(c["decode_steps"]):          # end-of-step state
+            minikv.append(dims, cache, kn, kn)
+        caches.append(cache)
+    q = torch.randn(B, Hq, D, device="cuda").half()
+    o = torch.empty_like(q)
+    ws = torch.zeros(minikv.decode_ws_bytes(dims, max(x.capacity for x in caches)),
+                     dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    alg = 0
+    for cache in caches:
+        minikv.decode_attn(dims, cache, q, o, ws)
+        alg += decode_bytes(c, cache.n_packed, cache.n_res)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "decode_calls": L,
+                      "algorithmic_bytes_per_call": alg / L}), flush=True)
 
 
 def decode_bytes(c, n_packed, n_res):
@@ -76,6 +149,9 @@ def prefill_flops(c):
 
 def main():
     args = parse()
+    if args.traffic_probe:
+        traffic_probe()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
               "path (each GPU would run the same kernels on its own share of "
@@ -279,7 +355,8 @@ def main():
                       "kernels), all layers, end-of-step cache state",
             "bound": "hbm", "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(args.config),
             "avg_launch_us": round(avg_dec_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": int(avg_dec_bytes),
             "launches": R * L,
