@@ -62,6 +62,25 @@ def test_decode_small(D, g, n, m):
     _decode_and_compare(torch, mk, dims, cache, oc, q)
 
 
+@pytest.mark.parametrize("D,g,Gk,Gv", [
+    (128, 1, 64, 32), (128, 4, 128, 64), (64, 2, 32, 64), (128, 8, 16, 128),
+    (64, 1, 128, 16), (128, 2, 32, 32), (64, 4, 64, 32)])
+def test_decode_group_sizes(D, g, Gk, Gv):
+    """Key groups of 16..128 tokens and value groups of 16..128 channels:
+    value groups wider than 16 channels repeat their scale per 16-channel
+    part; key groups wider than 16 tokens span several key tiles."""
+    torch, mk = require_gpu()
+    B, Hkv, n, m = 2, 2, 3000, 2100
+    say("decode-groups", dict(D=D, g=g, Gk=Gk, Gv=Gv))
+    dims, cache, oc = _build(torch, mk, B, Hkv, g, D, Gk, Gv, n, m,
+                             seed=7 * Gk + Gv + g)
+    for s_ in range(3):
+        q, kn, vn = synth.gen_decode_step(11, 0, s_, B, Hkv * g, Hkv, D)
+        mk.append(dims, cache, dev16(torch, kn), dev16(torch, vn))
+        oc.append(kn, vn)
+        _decode_and_compare(torch, mk, dims, cache, oc, q)
+
+
 def test_decode_group32_keys_and_residual_only():
     torch, mk = require_gpu()
     # tiny single-layer workload: D 64, 4 heads, key groups of 32 tokens
