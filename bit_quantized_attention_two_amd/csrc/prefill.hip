@@ -24,10 +24,11 @@
 namespace minikv {
 namespace {
 
-constexpr int kBM = 128;      // pass 1: queries per block (32 per wave)
+constexpr int kBM = 256;      // pass 1: queries per block (32 per wave)
 constexpr int kBN = 64;       // pass 1: keys per iteration
 constexpr int kBK2 = 128;     // pass 2: keys per block (32 per wave)
 constexpr int kBQ2 = 64;      // pass 2: queries per iteration
+constexpr float kLazy = 8.f;  // pass 1: log2 slack of the running max
 
 __device__ __forceinline__ half8_t load_h8(const uint16_t *p) {
     return *reinterpret_cast<const half8_t *>(p);
@@ -52,24 +53,49 @@ __device__ __forceinline__ half4_t ds_read_tr16(const uint16_t *lds) {
 
 template <bool B> struct bool_c { static constexpr bool value = B; };
 
+// Compile-time loop: f(integral_constant<int, i>) for i in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+constexpr int kPre = 4;       // pass 1: LDS fragment pairs requested ahead
+
+// max(x[l], x[l ^ 32]) in every lane l: v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second, so with both
+// operands equal to x, element 0 of the result holds the lower half twice
+// and element 1 the upper half twice.  The copy is hidden from the compiler
+// so that the swap of a value with itself is not folded.
+__device__ __forceinline__ float pair_max32(float x) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    asm volatile("" : "+v"(b));
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return __builtin_elementwise_maximum(__builtin_bit_cast(float, (unsigned)r[0]),
+                                         __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
 // ---------------------------------------------------------------- pass 1
 //
-// Per wave: 32 query rows.  S^T = K Q^T (keys as MFMA rows, queries as
-// columns) so that each lane owns one query column: the row max needs a
-// single exchange between the two lane halves.  O^T = V^T P^T re-uses the
-// S^T accumulator registers directly as the P operand: the contraction slots
-// of k-step (st, a2) are mapped onto the keys those registers hold, and the
-// matching V^T operand is read from the row-major V tile with the
-// transposing LDS read.
+// Block: 8 waves, 256 query rows; wave w owns 32 rows.  Per wave:
+// S^T = K Q^T (keys as MFMA rows, queries as columns) so that each lane owns
+// one query column and the row max needs a single exchange between the two
+// lane halves; O^T = V^T P^T re-uses the S^T accumulator registers directly
+// as the P operand, with the V^T operand read from the row-major V tile by
+// the transposing LDS read.
 //
-// Pipeline: the K/V tile of iteration kt+1 is loaded from HBM into registers
-// while tile kt is multiplied, then written to the other half of a
-// double-buffered LDS tile; one barrier per iteration.  Loads are never
-// predicated: rows past n re-read row n-1 and are masked.  Tiles that touch
-// the diagonal or the end of the sequence take a masked copy of the softmax;
-// the others a mask-free one.  Two waves per SIMD (<= 256 registers).
+// Two wave groups run in antiphase (ping-pong).  Group A = waves 0-3 and
+// group B = waves 4-7 share the four SIMDs pairwise.  Each wave alternates
+// an MFMA phase X(t) = {O += V(t-1) P(t-1); S(t) = K(t) Q^T} and a VALU phase
+// Y(t) = {softmax of S(t) -> P(t)}, with a block barrier after every phase;
+// group B starts one phase late, so that on every SIMD one wave multiplies
+// while the other one exponentiates.  Group A streams the K tiles and group
+// B the V tiles (global -> registers in X, registers -> LDS in Y); with the
+// phase offset, double-buffered K and V tiles are never written while a
+// wave may still read them.
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(
+__global__ __launch_bounds__(512, 1) void prefill_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o,
     float *__restrict__ lse, int Hq, int Hkv, int n, float sl2) {
@@ -77,24 +103,41 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(
     constexpr int DT = D / 32;
     constexpr int KPAD = D + 8;       // K row stride (halves): 4 dwords mod 64
     constexpr int VSTR = D + 32;      // V row stride (halves): 16 dwords mod 32
-    constexpr int LD = kBN * D / 8 / 256;          // uint4 loads per thread
+    constexpr int LD = kBN * D / 8 / 256;          // uint4 per thread of a group
     static_assert(LD >= 1 && LD * 256 * 8 == kBN * D, "tile / threads");
     __shared__ __attribute__((aligned(16))) uint16_t k_s[2][kBN * KPAD];
     __shared__ __attribute__((aligned(16))) uint16_t v_s[2][kBN * VSTR];
 
+    // Workgroups are dispatched in linear order (x fastest), round-robin
+    // over the 8 XCDs.  y walks the query blocks longest first; x walks the
+    // heads so that, with B*Hkv a multiple of 8, the g query heads of one kv
+    // head land on the same XCD (x mod 8) and share its L2 copy of K and V.
     const int nqb = (n + kBM - 1) / kBM;
-    const int qb = nqb - 1 - (int)blockIdx.x;       // longest rows first
-    const int bh = blockIdx.y;                      // b * Hq + hq
-    const int b = bh / Hq, hq = bh % Hq;
-    const int kvh = hq / (Hq / Hkv);
+    const int qb = nqb - 1 - (int)blockIdx.y;
+    const int g = Hq / Hkv;
+    const int units = (int)gridDim.x / g;           // B * Hkv
+    int u, j;
+    if (g > 1 && (units & 7) == 0) {
+        const int r = (int)blockIdx.x >> 3;
+        u = ((int)blockIdx.x & 7) + 8 * (r / g);
+        j = r % g;
+    } else {
+        u = (int)blockIdx.x / g;
+        j = (int)blockIdx.x % g;
+    }
+    const int b = u / Hkv, kvh = u % Hkv;
+    const int bh = b * Hq + kvh * g + j;
     const uint16_t *qp = q + (size_t)bh * n * D;
     const uint16_t *kp = k + ((size_t)b * Hkv + kvh) * n * D;
     const uint16_t *vp = v + ((size_t)b * Hkv + kvh) * n * D;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;                      // 0: group A, 1: group B
     const int l32 = lane & 31, hi = lane >> 5;
-    const int q0 = qb * kBM + wave * 32;
+    // the two waves of a SIMD (w, w + 4) own adjacent 32-row slices
+    const int q0 = qb * kBM + (wave & 3) * 64 + grp * 32;
     const int qrow = q0 + l32;
 
     half8_t qf[KS];
@@ -108,73 +151,119 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(
     float l_run = 0.f;
 
     const int kend = min(n, qb * kBM + kBM);
-    const int ntiles = (kend + kBN - 1) / kBN;
+    const int T = (kend + kBN - 1) / kBN;           // tiles of the block
+    const int Tw = q0 < n ? min(T, (q0 + 31) / kBN + 1) : 0;   // of this wave
 
-    u32x4 kreg[LD], vreg[LD];
-    auto load_tile = [&](int k0) __attribute__((always_inline)) {
+    // group A stages K tiles, group B V tiles
+    const int gt = tid & 255;
+    const uint16_t *src = grp ? vp : kp;
+    u32x4 stage[LD];
+    auto load_tile = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
-            const int idx = tid + 256 * i;
+            const int idx = gt + 256 * i;
             const int r = idx / (D / 8), cc = idx % (D / 8);
-            const size_t off = (size_t)min(k0 + r, n - 1) * D + cc * 8;
-            kreg[i] = *reinterpret_cast<const u32x4 *>(kp + off);
-            vreg[i] = *reinterpret_cast<const u32x4 *>(vp + off);
+            stage[i] = *reinterpret_cast<const u32x4 *>(
+                src + (size_t)min(t * kBN + r, n - 1) * D + cc * 8);
         }
     };
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    auto store_tile = [&](int t) __attribute__((always_inline)) {
+        uint16_t *dst = grp ? v_s[t & 1] : k_s[t & 1];
+        const int stride = grp ? VSTR : KPAD;
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
-            const int idx = tid + 256 * i;
+            const int idx = gt + 256 * i;
             const int r = idx / (D / 8), cc = idx % (D / 8);
-            *reinterpret_cast<u32x4 *>(k_s[buf] + r * KPAD + cc * 8) = kreg[i];
-            *reinterpret_cast<u32x4 *>(v_s[buf] + r * VSTR + cc * 8) = vreg[i];
+            *reinterpret_cast<u32x4 *>(dst + r * stride + cc * 8) = stage[i];
         }
     };
 
-    // lane-constant parts of the transposed V reads
-    const int grp = lane >> 4, L = lane & 15;
-    const int v_lane_off = (4 * (grp >> 1) + (L >> 2)) * VSTR + 16 * (grp & 1) + 4 * (L & 3);
+    // lane-constant part of the transposed V reads
+    const int vg = lane >> 4, L = lane & 15;
+    const int v_lane_off = (4 * (vg >> 1) + (L >> 2)) * VSTR + 16 * (vg & 1) + 4 * (L & 3);
 
-    auto tile_step = [&](auto MASKED, int buf, int k0) __attribute__((always_inline)) {
-        float16_t s[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            s[st] = float16_t{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const half8_t a =
-                    load_h8(k_s[buf] + (st * 32 + l32) * KPAD + ks * 16 + 8 * hi);
-                s[st] = mfma32(a, qf[ks], s[st]);
+    float16_t s[2];
+    half8_t pf[4];                                  // k-step (st, a2) = 2 st + a2
+
+    // MFMA phase: S = K(tq) Q^T and/or O += V(tp) P, issued as pairs of one
+    // QK and one PV step; the LDS fragments of pair i + kPre are requested
+    // while pair i multiplies, and a scheduling fence after every pair keeps
+    // the compiler from bunching the reads.
+    auto xphase = [&](auto DO_QK, auto DO_PV, int tq, int tp) __attribute__((always_inline)) {
+        constexpr bool dq = decltype(DO_QK)::value, dp = decltype(DO_PV)::value;
+        constexpr int NQ = 2 * KS;                  // QK steps (ks, st)
+        constexpr int NV = 4 * DT;                  // PV steps (kk, dt)
+        constexpr int N = NQ > NV ? NQ : NV;
+        const uint16_t *kb = k_s[tq & 1] + l32 * KPAD + 8 * hi;
+        const uint16_t *vb = v_s[tp & 1] + v_lane_off;
+        half8_t kf[kPre];
+        half4_t vf0[kPre], vf1[kPre];
+        auto req = [&](auto I) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value;
+            if constexpr (dq && i < NQ) {
+                constexpr int st = i & 1, ks = i >> 1;
+                kf[i % kPre] = load_h8(kb + st * 32 * KPAD + ks * 16);
             }
+            if constexpr (dp && i < NV) {
+                constexpr int kk = i / DT, dt = i % DT;
+                const uint16_t *vk = vb + ((kk >> 1) * 32 + 16 * (kk & 1)) * VSTR + dt * 32;
+                vf0[i % kPre] = ds_read_tr16(vk);
+                vf1[i % kPre] = ds_read_tr16(vk + 8 * VSTR);
+            }
+        };
+        if constexpr (dq) {
+            s[0] = float16_t{};
+            s[1] = float16_t{};
         }
-        // s[st][i] = S[key = k0 + 32 st + 8(i/4) + 4 hi + i%4][query = qrow]
-        if constexpr (decltype(MASKED)::value) {
+        static_for<0, kPre>([&](auto I) __attribute__((always_inline)) { req(I); });
+        static_for<0, N>([&](auto I) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value;
+            if constexpr (dq && i < NQ)
+                s[i & 1] = mfma32(kf[i % kPre], qf[i >> 1], s[i & 1]);
+            if constexpr (dp && i < NV) {
+                const half8_t a = __builtin_shufflevector(vf0[i % kPre], vf1[i % kPre],
+                                                          0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[i % DT] = mfma32(a, pf[i / DT], oacc[i % DT]);
+            }
+            req(std::integral_constant<int, i + kPre>{});
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // s[st][i] = S[key = k0 + 32 st + 8(i/4) + 4 hi + i%4][query = qrow]
+    auto softmax = [&](int t) __attribute__((always_inline)) {
+        const int k0 = t * kBN;
+        if ((k0 + kBN - 1 > q0) || (k0 + kBN > n)) {   // diagonal or tail tile
+            // key k0 + 4 hi + c is kept iff it is <= qrow and < n
+            const int lim = min(qrow, n - 1) - k0 - 4 * hi;
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + st * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    if (key > qrow || key >= n) s[st][i] = -INFINITY;
-                }
+                for (int i = 0; i < 16; ++i)
+                    if (st * 32 + 8 * (i >> 2) + (i & 3) > lim) s[st][i] = -INFINITY;
         }
-        float tmax = -INFINITY;
+        // NaN-propagating maximum: no canonicalisation of the MFMA results
+        float t0 = -INFINITY, t1 = -INFINITY;
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(s[st][i], s[st][i + 1]));
-        tmax = fmaxf(tmax, shfl_xor(tmax, 32)) * sl2;
+            for (int i = 0; i < 16; i += 4) {
+                t0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(t0, s[st][i]), s[st][i + 1]);
+                t1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(t1, s[st][i + 2]), s[st][i + 3]);
+            }
+        float tmax = __builtin_elementwise_maximum(t0, t1);
+        tmax = pair_max32(tmax) * sl2;
         const float m_new = fmaxf(m_run, tmax);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        // rescale only when some row max of the wave moved
-        if (__ballot(m_new > m_run) != 0) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        // Lazy rescale: the running max moves only when some row of the
+        // wave grew by more than 2^kLazy; otherwise p may exceed 1 by at
+        // most that factor (exact in fp32, far from fp16 overflow).
+        if (__ballot(m_new > m_run + kLazy) != 0) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
             l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            m_run = m_new;
         }
-        m_run = m_new;
-
-        half8_t pf[4];                              // k-step (st, a2) = 2 st + a2
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         float l0 = 0.f, l1 = 0.f;                   // tile sum first: no drift
 #pragma unroll
         for (int st = 0; st < 2; ++st)
@@ -188,39 +277,57 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd_kernel(
                 pf[st * 2 + (i >> 3)][(i & 7) + 1] = (half_t)p1;
             }
         l_run += l0 + l1;
-        const uint16_t *vb = v_s[buf] + v_lane_off;
+    };
+    // Phase fences: empty asm statements that read (and claim to modify) the
+    // registers handed from one phase to the next, so that no part of a
+    // phase's arithmetic is moved across the block barrier into the other.
+    auto bar_x = [&]() __attribute__((always_inline)) {    // end of X
+        __syncthreads();
+        asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+    };
+    auto bar_y = [&]() __attribute__((always_inline)) {    // end of Y
+        asm volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]), "+v"(pf[3]), "+v"(l_run));
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int st = kk >> 1, a2 = kk & 1;
-            const uint16_t *vk = vb + (st * 32 + 16 * a2) * VSTR;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const half4_t lo4 = ds_read_tr16(vk + dt * 32);
-                const half4_t hi4 = ds_read_tr16(vk + 8 * VSTR + dt * 32);
-                const half8_t a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3,
-                                                          4, 5, 6, 7);
-                oacc[dt] = mfma32(a, pf[kk], oacc[dt]);
-            }
-        }
+        for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+v"(oacc[dt]));
+        __syncthreads();
     };
 
+    // Phases of one wave: X(0) Y(0) X(1) ... Y(T-1) X(T), each followed by a
+    // block barrier; the wave computes only for its own tiles t < Tw.
     load_tile(0);
     store_tile(0);
     __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int buf = kt & 1;
-        const int k0 = kt * kBN;
-        const bool more = kt + 1 < ntiles;
-        if (more) load_tile(k0 + kBN);
-        if (k0 <= q0 + 31) {                        // not fully masked
-            if ((k0 + kBN - 1 > q0) || (k0 + kBN > n))
-                tile_step(bool_c<true>{}, buf, k0);
-            else
-                tile_step(bool_c<false>{}, buf, k0);
+    if (grp == 1) __syncthreads();                  // group B: one phase late
+    if (T > 1) load_tile(1);
+    int t = 0;
+    if (Tw > 0) {
+        xphase(bool_c<true>{}, bool_c<false>{}, 0, 0);
+        bar_x();
+        for (; t + 1 < Tw; ++t) {
+            softmax(t);                             // Y(t)
+            if (t + 1 < T) store_tile(t + 1);
+            bar_y();
+            // X(t+1)
+            if (t + 2 < T) load_tile(t + 2);
+            xphase(bool_c<true>{}, bool_c<true>{}, t + 1, t);
+            bar_x();
         }
-        if (more) store_tile(buf ^ 1);
+        softmax(t);                                 // Y(Tw-1)
+        if (t + 1 < T) store_tile(t + 1);
+        bar_y();
+        // X(Tw)
+        if (t + 2 < T) load_tile(t + 2);
+        xphase(bool_c<false>{}, bool_c<true>{}, 0, t);
+        ++t;
+    }
+    bar_x();
+    for (; t < T; ++t) {                            // idle phases: staging only
+        if (t + 1 < T) store_tile(t + 1);
+        __syncthreads();
+        if (t + 2 < T) load_tile(t + 2);
         __syncthreads();
     }
+    if (grp == 0) __syncthreads();                  // group A: match B's count
 
     const float l_tot = l_run + shfl_xor(l_run, 32);
     if (qrow < n) {
@@ -262,8 +369,8 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t q_s[2][kBQ2 * QPAD];
     __shared__ __attribute__((aligned(16))) float lse_s[2][kBQ2];
 
-    const int kb = blockIdx.x;                      // block 0 has most rows
-    const int unit = blockIdx.y;                    // b * Hkv + kvh
+    const int kb = blockIdx.y;                      // block 0 has most rows
+    const int unit = blockIdx.x;                    // b * Hkv + kvh
     const int b = unit / Hkv, kvh = unit % Hkv;
     const int g = Hq / Hkv;
     const int tid = threadIdx.x;
@@ -379,13 +486,13 @@ hipError_t launch_prefill(const uint16_t *q, const uint16_t *k,
                           float *col, int B, int Hq, int Hkv, int n, int D,
                           hipStream_t stream) {
     const float sl2 = kLog2e / sqrtf((float)D);
-    dim3 g1((n + kBM - 1) / kBM, B * Hq);
-    dim3 g2((n + kBK2 - 1) / kBK2, B * Hkv);
+    dim3 g1(B * Hq, (n + kBM - 1) / kBM);
+    dim3 g2(B * Hkv, (n + kBK2 - 1) / kBK2);
     if (D == 128) {
-        prefill_fwd_kernel<128><<<g1, 256, 0, stream>>>(q, k, v, o, lse, Hq, Hkv, n, sl2);
+        prefill_fwd_kernel<128><<<g1, 512, 0, stream>>>(q, k, v, o, lse, Hq, Hkv, n, sl2);
         prefill_col_kernel<128><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
     } else {
-        prefill_fwd_kernel<64><<<g1, 256, 0, stream>>>(q, k, v, o, lse, Hq, Hkv, n, sl2);
+        prefill_fwd_kernel<64><<<g1, 512, 0, stream>>>(q, k, v, o, lse, Hq, Hkv, n, sl2);
         prefill_col_kernel<64><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
     }
     return hipGetLastError();
