@@ -26,7 +26,6 @@ namespace {
 
 constexpr int kBM = 256;      // pass 1: queries per block (32 per wave)
 constexpr int kBN = 64;       // pass 1: keys per iteration
-constexpr int kBK2 = 128;     // pass 2: keys per block (32 per wave)
 constexpr int kBQ2 = 64;      // pass 2: queries per iteration
 constexpr float kLazy = 8.f;  // pass 1: log2 slack of the running max
 
@@ -350,15 +349,22 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_kernel(
 
 // ---------------------------------------------------------------- pass 2
 //
-// Per wave: 32 key columns, K^T held in registers as the MFMA B operand.
-// S = Q K^T with queries as rows: each lane owns one key column and adds the
-// probabilities of its 16 query rows per 32-row sub-tile; the two lane halves
-// are combined once at the end.  The next 64-query tile (and its LSE) is
-// loaded into registers while the current one is used, into a double-buffered
-// LDS tile, with one barrier per tile.  Rows past n get LSE = +inf, so their
-// probabilities are exactly 0; only sub-tiles that cross the diagonal take
-// the masked copy of the update.
-template <int D>
+// Per wave: NC groups of 32 key columns, K^T of each held in registers as
+// an MFMA B operand, so that every Q fragment read from LDS feeds NC MFMAs
+// (NC = 2 halves the LDS reads per flop; NC = 1 gives twice the workgroups
+// for short sequences).  S = Q K^T with queries as rows: each lane owns one key
+// column per group and adds the probabilities of its 16 query rows per
+// 32-row sub-tile; the two lane halves are combined once at the end.  The
+// query tiles of the g heads of the kv head are walked as one flat sequence
+// of 64-row tiles, each split into two 32-row sub-tiles j.  Software
+// pipeline over sub-tiles: the MFMAs of sub-tile j+1 are issued before the
+// exponentials of sub-tile j.  Q tiles (and their LSE) go global ->
+// registers -> a three-slot LDS ring two tiles ahead of use, so the next
+// tile is resident when its first MFMAs issue; one barrier per tile.  Rows
+// past n get LSE = +inf, so their probabilities are exactly 0; sub-tiles
+// that reach the diagonal are masked (all of a sub-tile whose rows precede
+// the wave's keys is masked to 0).
+template <int D, int NC>
 __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const float *__restrict__ lse, float *__restrict__ col, int Hq, int Hkv,
@@ -366,38 +372,43 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
     constexpr int KS = D / 16;
     constexpr int QPAD = D + 8;
     constexpr int QLD = kBQ2 * D / 8 / 256;         // uint4 loads per thread
-    __shared__ __attribute__((aligned(16))) uint16_t q_s[2][kBQ2 * QPAD];
-    __shared__ __attribute__((aligned(16))) float lse_s[2][kBQ2];
+    __shared__ __attribute__((aligned(16))) uint16_t q_s[3][kBQ2 * QPAD];
+    __shared__ __attribute__((aligned(16))) float lse_s[3][kBQ2];
 
     const int kb = blockIdx.y;                      // block 0 has most rows
     const int unit = blockIdx.x;                    // b * Hkv + kvh
     const int b = unit / Hkv, kvh = unit % Hkv;
     const int g = Hq / Hkv;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
-    const int k0w = kb * kBK2 + wave * 32;
-    const int key = k0w + l32;
+    const int k0w = (kb * 4 + wave) * 32 * NC;      // first key of the wave
     const uint16_t *kp = k + (size_t)unit * n * D;
 
-    half8_t kf[KS];
+    half8_t kf[NC][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        kf[ks] = load_h8(kp + (size_t)min(key, n - 1) * D + ks * 16 + 8 * hi);
-    // Column sum: each 64-row tile is summed on its own, then added to a
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kf[c][ks] = load_h8(kp + (size_t)min(k0w + 32 * c + l32, n - 1) * D + ks * 16 + 8 * hi);
+    // Column sums: each 64-row tile is summed on its own, then added to a
     // compensated (Kahan) running sum, so tens of thousands of small
     // probabilities added to a large column total do not drift low.
-    float colacc = 0.f, colcomp = 0.f;
+    float colacc[NC], colcomp[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) colacc[c] = colcomp[c] = 0.f;
 
     // flattened (head, query tile) sequence
-    const int qstart = kb * kBK2;
+    const int qstart = kb * 128 * NC;
     const int tiles_per_head = (n - qstart + kBQ2 - 1) / kBQ2;
     const int ntiles = g * tiles_per_head;
     u32x4 qreg[QLD];
     float lreg = 0.f;
+    auto tile_q0 = [&](int t) { return qstart + (t % tiles_per_head) * kBQ2; };
     auto load_tile = [&](int t) __attribute__((always_inline)) {
         const int h = t / tiles_per_head;
-        const int qt0 = qstart + (t % tiles_per_head) * kBQ2;
+        const int qt0 = tile_q0(t);
         const size_t bhq = (size_t)b * Hq + kvh * g + h;
         const uint16_t *qp = q + bhq * n * D;
 #pragma unroll
@@ -412,7 +423,8 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
             lreg = qt0 + tid < n ? x : INFINITY;
         }
     };
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    auto store_tile = [&](int t) __attribute__((always_inline)) {
+        const int buf = t % 3;
 #pragma unroll
         for (int i = 0; i < QLD; ++i) {
             const int idx = tid + 256 * i;
@@ -422,61 +434,94 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
         if (tid < kBQ2) lse_s[buf][tid] = lreg;
     };
 
-    auto sub_tile = [&](auto MASKED, int buf, int qt0, int qs) __attribute__((always_inline)) -> float {
-        float16_t s = float16_t{};
+    // sub-tile j = 2 t + qs: rows tile_q0(t) + 32 qs .. + 31
+    auto mfma_sub = [&](int j, float16_t (&acc)[NC]) __attribute__((always_inline)) {
+        const uint16_t *qb = q_s[(j >> 1) % 3] + ((j & 1) * 32 + l32) * QPAD + 8 * hi;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] = float16_t{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const half8_t a =
-                load_h8(q_s[buf] + (qs * 32 + l32) * QPAD + ks * 16 + 8 * hi);
-            s = mfma32(a, kf[ks], s);
+            const half8_t a = load_h8(qb + ks * 16);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[c] = mfma32(a, kf[c][ks], acc[c]);
         }
-        // s[i] = S[query = qt0 + 32 qs + 8(i/4) + 4 hi + i%4][key]
-        float t0 = 0.f, t1 = 0.f;
+    };
+    // acc[c][i] = S[query = q0 + 8(i/4) + 4 hi + i%4][key k0w + 32 c + l32]
+    auto exp_sum = [&](int j, const float16_t (&acc)[NC], float (&tile)[NC]) __attribute__((always_inline)) {
+        const float *lb = lse_s[(j >> 1) % 3] + (j & 1) * 32 + 4 * hi;
+        const int q0 = tile_q0(j >> 1) + (j & 1) * 32;
+        float p[NC][16];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-            const float4_t l4 = *reinterpret_cast<const float4_t *>(
-                &lse_s[buf][qs * 32 + 8 * i4 + 4 * hi]);
+            const float4_t l4 = *reinterpret_cast<const float4_t *>(lb + 8 * i4);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * i4 + j], sl2, -l4[j]));
-                if constexpr (decltype(MASKED)::value) {
-                    if (qt0 + qs * 32 + 8 * i4 + 4 * hi + j < key) p = 0.f;
-                }
-                if (j & 1) t1 += p; else t0 += p;
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    p[c][4 * i4 + jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[c][4 * i4 + jj], sl2, -l4[jj]));
+        }
+        if (q0 < k0w + 32 * NC - 1) {               // reaches the wave's diagonal
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int lim = k0w + 32 * c + l32 - q0 - 4 * hi;   // keep row offset >= lim
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (8 * (i >> 2) + (i & 3) < lim) p[c][i] = 0.f;
             }
         }
-        return t0 + t1;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                t0 += p[c][i];
+                t1 += p[c][i + 1];
+            }
+            tile[c] += t0 + t1;
+        }
     };
 
     if (ntiles > 0) {
         load_tile(0);
         store_tile(0);
+        if (ntiles > 1) {
+            load_tile(1);
+            store_tile(1);
+        }
     }
     __syncthreads();
+    // sub-tiles 2t (s0) and 2t + 1 (s1) of tile t; the MFMAs of the next
+    // sub-tile are issued ahead of the exponentials of the current one.  At
+    // the last tile the look-ahead reads a stale slot (in bounds, unused).
+    float16_t s0[NC], s1[NC];
+    if (ntiles > 0) mfma_sub(0, s0);
     for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        const int qt0 = qstart + (t % tiles_per_head) * kBQ2;
-        const bool more = t + 1 < ntiles;
-        if (more) load_tile(t + 1);
-        if (qt0 + kBQ2 - 1 >= k0w) {               // some query sees some key
-            float tile = 0.f;
+        const bool more = t + 2 < ntiles;
+        if (more) load_tile(t + 2);
+        const int j = 2 * t;
+        float tile[NC];
 #pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
-                if (qt0 + qs * 32 < k0w + 31)       // crosses the diagonal
-                    tile += sub_tile(bool_c<true>{}, buf, qt0, qs);
-                else
-                    tile += sub_tile(bool_c<false>{}, buf, qt0, qs);
-            }
-            const float y = tile - colcomp;
-            const float tt = colacc + y;
-            colcomp = (tt - colacc) - y;
-            colacc = tt;
+        for (int c = 0; c < NC; ++c) tile[c] = 0.f;
+        mfma_sub(j + 1, s1);
+        exp_sum(j, s0, tile);
+        mfma_sub(j + 2, s0);                        // first sub-tile of tile t+1
+        exp_sum(j + 1, s1, tile);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {              // Kahan add of the tile sums
+            const float y = tile[c] - colcomp[c];
+            const float tt = colacc[c] + y;
+            colcomp[c] = (tt - colacc[c]) - y;
+            colacc[c] = tt;
         }
-        if (more) store_tile(buf ^ 1);
+        if (more) store_tile(t + 2);
         __syncthreads();
     }
-    colacc += shfl_xor(colacc, 32);
-    if (hi == 0 && key < n) col[(size_t)unit * n + key] = colacc;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const float tot = colacc[c] + shfl_xor(colacc[c], 32);
+        const int key = k0w + 32 * c + l32;
+        if (hi == 0 && key < n) col[(size_t)unit * n + key] = tot;
+    }
 }
 
 }  // namespace
@@ -486,14 +531,23 @@ hipError_t launch_prefill(const uint16_t *q, const uint16_t *k,
                           float *col, int B, int Hq, int Hkv, int n, int D,
                           hipStream_t stream) {
     const float sl2 = kLog2e / sqrtf((float)D);
-    dim3 g1(B * Hq, (n + kBM - 1) / kBM);
-    dim3 g2(B * Hkv, (n + kBK2 - 1) / kBK2);
+    const dim3 g1(B * Hq, (n + kBM - 1) / kBM);
+    // Pass 2 with 64 keys per wave unless that leaves too few workgroups
+    // (short sequences) to balance the triangular work over the CUs.
+    const bool wide = (long)B * Hkv * ((n + 255) / 256) >= 1024;
+    const dim3 g2(B * Hkv, (n + (wide ? 255 : 127)) / (wide ? 256 : 128));
     if (D == 128) {
         prefill_fwd_kernel<128><<<g1, 512, 0, stream>>>(q, k, v, o, lse, Hq, Hkv, n, sl2);
-        prefill_col_kernel<128><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
+        if (wide)
+            prefill_col_kernel<128, 2><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
+        else
+            prefill_col_kernel<128, 1><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
     } else {
         prefill_fwd_kernel<64><<<g1, 512, 0, stream>>>(q, k, v, o, lse, Hq, Hkv, n, sl2);
-        prefill_col_kernel<64><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
+        if (wide)
+            prefill_col_kernel<64, 2><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
+        else
+            prefill_col_kernel<64, 1><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
     }
     return hipGetLastError();
 }

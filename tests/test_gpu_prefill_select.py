@@ -66,6 +66,30 @@ def test_prefill_small_all_units(B, Hq, Hkv, D, n):
     np.testing.assert_allclose(col.sum(-1), g * n, rtol=1e-4)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,n", [(8, 32, 32, 1000), (16, 8, 4, 4000)])
+def test_prefill_many_units(B, Hq, Hkv, n):
+    """Enough units and keys that pass 2 takes its 64-keys-per-wave form;
+    four units (first, last, two inner) are compared on every row and
+    column, and every unit must satisfy sum(col) = g n."""
+    torch, mk = require_gpu()
+    D = 128
+    assert B * Hkv * ((n + 255) // 256) >= 1024
+    q, k, v = [], [], []
+    for b in range(B):
+        a = synth.gen_unit_batch(2, 0, b, Hq, Hkv, n, D, n // 4)
+        q.append(a[0]); k.append(a[1]); v.append(a[2])
+    q, k, v = np.stack(q), np.stack(k), np.stack(v)
+    say("prefill-many", dict(B=B, Hq=Hq, Hkv=Hkv, D=D, n=n))
+    o, lse, col = _prefill(torch, mk, q, k, v)
+    g = Hq // Hkv
+    np.testing.assert_allclose(col.sum(-1), g * n, rtol=1e-4)
+    units = [(0, 0), (B - 1, Hkv - 1), (B // 2, 1), (1, Hkv // 2)]
+    for (b, h), (ro, rl, rc) in zip(units, _oracle_units(q, k, v, units)):
+        assert_close(o[b, h * g:(h + 1) * g], ro, "O b%d h%d" % (b, h))
+        assert_close(lse[b, h * g:(h + 1) * g], rl, "LSE b%d h%d" % (b, h))
+        assert_close(col[b, h], rc, "col b%d h%d" % (b, h))
+
+
 @pytest.mark.parametrize("cfg_id,full_units,rows", [(2, 2, 48), (4, 1, 24),
                                                     (5, 1, 12)])
 def test_prefill_full_size(cfg_id, full_units, rows):
