@@ -29,7 +29,7 @@
 // channel row keeps the column of its own group.  The z terms: per key
 // group an MFMA of the zero-points with q, and per token a VALU sum.
 //
-// Work split: block (split, unit) covers `chunk` packed tokens of one unit,
+// Work split: block (unit, split) covers `chunk` packed tokens of one unit,
 // each of its 4 waves a quarter of them; the last split of a unit is its
 // fp16 residual when it has one.  A wave computes all its logits (phase K),
 // its softmax statistics, then P.V (phase V); the block merges its waves in
@@ -663,8 +663,11 @@ __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0
 // FULLV: value channel groups of 16 (D/16 scales per token).
 template <int D, int G, bool FULLV>
 __global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_kernel(DecArgs a) {
-    const int unit = blockIdx.y;
-    const int split = blockIdx.x;
+    // x = unit, y = split: with the round-robin dispatch of workgroups over
+    // the 8 XCDs, every split of a unit (and its merge below) runs on the
+    // XCD unit mod 8 when the unit count is a multiple of 8.
+    const int unit = blockIdx.x;
+    const int split = blockIdx.y;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -738,7 +741,7 @@ __global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_k
 }
 
 // Merge the splits of one (unit, head): o = sum_s 2^(m_s - M) o_s / L.
-// Block (head, unit); thread (slice, channel) takes every SLICES-th split of
+// Block (unit, head); thread (slice, channel) takes every SLICES-th split of
 // one channel.  It loads a batch of up to NB splits' (max, sum, o) at once
 // and folds it into a running (max, sum, o); the slices are then merged in
 // LDS.  A workload with at most SLICES * NB splits per unit needs a single
@@ -750,8 +753,8 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     constexpr int SLICES = kThreads / D;
     constexpr int NB = 8;
     __shared__ float r_m[kThreads], r_l[kThreads], r_o[kThreads];
-    const int h = blockIdx.x;
-    const int unit = blockIdx.y;
+    const int unit = blockIdx.x;
+    const int h = blockIdx.y;
     const int tid = threadIdx.x;
     const int ch = tid % D, slice = tid / D;
     const float *ml = part_ml + (size_t)unit * nsplit * G * 2 + h * 2;
@@ -826,10 +829,10 @@ int pick_chunk(int units, int n_packed, int Gk, int g) {
 template <int D, int G>
 hipError_t launch_decode_dg(const DecArgs &a, int units, hipStream_t stream) {
     if (a.c.Gv == 16)
-        decode_kernel<D, G, true><<<dim3(a.nsplit, units), kThreads, 0, stream>>>(a);
+        decode_kernel<D, G, true><<<dim3(units, a.nsplit), kThreads, 0, stream>>>(a);
     else
-        decode_kernel<D, G, false><<<dim3(a.nsplit, units), kThreads, 0, stream>>>(a);
-    decode_combine_kernel<D, G><<<dim3(G, units), kThreads, 0, stream>>>(
+        decode_kernel<D, G, false><<<dim3(units, a.nsplit), kThreads, 0, stream>>>(a);
+    decode_combine_kernel<D, G><<<dim3(units, G), kThreads, 0, stream>>>(
         a.part_ml, a.part_o, a.nsplit, a.o);
     return hipGetLastError();
 }
