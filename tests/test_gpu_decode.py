@@ -108,6 +108,35 @@ def test_decode_after_appends_and_determinism():
             assert np.array_equal(o1.view(np.uint16), o2.view(np.uint16))
 
 
+@pytest.mark.parametrize("Hkv", [4, 3])
+def test_decode_shared_workspace(Hkv):
+    """Two caches of different capacities and a residual-only one, with the
+    same dims, share one workspace across interleaved calls (plain and
+    fused-append forms): every call must match the oracle."""
+    torch, mk = require_gpu()
+    B, g, D = 2, 2, 128
+    say("decode-shared-ws", dict(B=B, Hkv=Hkv, g=g))
+    a = _build(torch, mk, B, Hkv, g, D, 16, 16, 1500, 900, seed=21)
+    b = _build(torch, mk, B, Hkv, g, D, 16, 16, 3000, 2100, seed=22)
+    c = _build(torch, mk, B, Hkv, g, D, 16, 16, 40, 9, seed=23)   # residual only
+    dims = a[0]
+    ws = torch.zeros(max(mk.decode_ws_bytes(dims, x[1].capacity) for x in (a, b, c)),
+                     dtype=torch.uint8, device="cuda")
+    for s in range(6):
+        for (_, cache, oc) in ((a if s % 2 else b), c, (b if s % 2 else a)):
+            q, kn, vn = synth.gen_decode_step(24, 0, s, B, Hkv * g, Hkv, D)
+            if s >= 3:
+                o = mk.append_decode(dims, cache, dev16(torch, kn), dev16(torch, vn),
+                                     dev16(torch, q), ws=ws).cpu().numpy()
+                oc.append(kn, vn)
+            else:
+                o = mk.decode_attn(dims, cache, dev16(torch, q), ws=ws).cpu().numpy()
+            units = [(bb, h) for bb in range(B) for h in range(Hkv)]
+            for (bb, h) in units:
+                ref = oc.decode_unit(q[bb, h * g:(h + 1) * g], bb, h)
+                assert_close(o[bb, h * g:(h + 1) * g], ref, "s%d b%d h%d" % (s, bb, h))
+
+
 def test_decode_empty_cache_is_an_error():
     torch, mk = require_gpu()
     dims = mk.make_dims(1, 2, 2, 128)
