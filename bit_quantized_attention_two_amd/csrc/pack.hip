@@ -63,8 +63,8 @@ __device__ __forceinline__ void unpack8(uint4 x, float *f) {
 }
 
 // Keys: one thread per (key group, 8 channels), 16-byte loads of each of the
-// group's Gk source rows (read twice: min/max, then codes; the second read
-// hits the cache).  A key word holds 16 channels of one token, so the two
+// group's Gk source rows, eight rows in flight at a time (read twice:
+// min/max, then codes; the second read hits the cache).  A key word holds 16 channels of one token, so the two
 // threads of a 16-channel block combine their halves of each word.
 template <int D>
 __global__ __launch_bounds__(256) void pack_keys_kernel(
@@ -81,19 +81,32 @@ __global__ __launch_bounds__(256) void pack_keys_kernel(
                                  : nullptr;
     const int p0 = gi * Gk;
 
-    float mn[8], mx[8];
-    for (int t = 0; t < Gk; ++t) {
-        const int row = sel ? sel[p0 + t] : p0 + t;
-        float x[8];
-        unpack8(*reinterpret_cast<const uint4 *>(base + (size_t)row * D), x);
+    // rows are loaded RB at a time, so that their latencies overlap
+    constexpr int RB = 8;                        // Gk is a multiple of 16
+    auto load_rows = [&](int t0, uint4 (&r)[RB]) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (t == 0) {
-                mn[j] = x[j];
-                mx[j] = x[j];
-            } else {
-                if (x[j] < mn[j]) mn[j] = x[j];
-                if (x[j] > mx[j]) mx[j] = x[j];
+        for (int i = 0; i < RB; ++i) {
+            const int row = sel ? sel[p0 + t0 + i] : p0 + t0 + i;
+            r[i] = *reinterpret_cast<const uint4 *>(base + (size_t)row * D);
+        }
+    };
+    float mn[8], mx[8];
+    for (int t0 = 0; t0 < Gk; t0 += RB) {
+        uint4 rr[RB];
+        load_rows(t0, rr);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            float x[8];
+            unpack8(rr[i], x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (t0 + i == 0) {
+                    mn[j] = x[j];
+                    mx[j] = x[j];
+                } else {
+                    if (x[j] < mn[j]) mn[j] = x[j];
+                    if (x[j] > mx[j]) mx[j] = x[j];
+                }
             }
         }
     }
@@ -105,15 +118,19 @@ __global__ __launch_bounds__(256) void pack_keys_kernel(
     int32_t *kq = c.kq + (size_t)unit * c.kq_unit() +
                   (size_t)g_out * Gk * (D / 16) + oct / 2;
     const int sh = 16 * (oct & 1);               // this thread's half-word
-    for (int t = 0; t < Gk; ++t) {
-        const int row = sel ? sel[p0 + t] : p0 + t;
-        float x[8];
-        unpack8(*reinterpret_cast<const uint4 *>(base + (size_t)row * D), x);
-        uint32_t half = 0;
+    for (int t0 = 0; t0 < Gk; t0 += RB) {
+        uint4 rr[RB];
+        load_rows(t0, rr);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) half |= code_of(x[j], qp[j]) << (sh + 2 * j);
-        const uint32_t word = half | (uint32_t)__shfl_xor((int)half, 1);
-        if ((oct & 1) == 0) kq[(size_t)t * (D / 16)] = (int32_t)word;
+        for (int i = 0; i < RB; ++i) {
+            float x[8];
+            unpack8(rr[i], x);
+            uint32_t half = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) half |= code_of(x[j], qp[j]) << (sh + 2 * j);
+            const uint32_t word = half | (uint32_t)__shfl_xor((int)half, 1);
+            if ((oct & 1) == 0) kq[(size_t)(t0 + i) * (D / 16)] = (int32_t)word;
+        }
     }
     const size_t mo = (size_t)unit * c.km_unit() + (size_t)g_out * D + oct * 8;
     uint32_t sw[4], zw[4];
