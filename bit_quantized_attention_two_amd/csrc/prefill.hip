@@ -108,21 +108,35 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t v_s[2][kBN * VSTR];
 
     // Workgroups are dispatched in linear order (x fastest), round-robin
-    // over the 8 XCDs.  y walks the query blocks longest first; x walks the
-    // heads so that, with B*Hkv a multiple of 8, the g query heads of one kv
-    // head land on the same XCD (x mod 8) and share its L2 copy of K and V.
+    // over the 8 XCDs.  By default y walks the query blocks longest first
+    // and x the heads, so that, with B*Hkv a multiple of 8, the g query
+    // heads of one kv head land on the same XCD (x mod 8) and share its L2
+    // copy of K and V.
     const int nqb = (n + kBM - 1) / kBM;
-    const int qb = nqb - 1 - (int)blockIdx.y;
     const int g = Hq / Hkv;
     const int units = (int)gridDim.x / g;           // B * Hkv
-    int u, j;
-    if (g > 1 && (units & 7) == 0) {
+    int u, j, qb;
+    if ((units & 7) == 0 && units >= 64) {
+        // Many units: each XCD runs the blocks of one unit after another
+        // (longest first within the unit), so the blocks it holds at once
+        // stream the same K and V through its L2 instead of 32 different
+        // heads' worth from HBM; with >= 8 units per XCD the tail this adds
+        // is a small part of the run.
+        const int L = (int)blockIdx.y * (int)gridDim.x + (int)blockIdx.x;
+        const int s = L >> 3, per_unit = nqb * g;
+        const int rem = s % per_unit;
+        u = (L & 7) + 8 * (s / per_unit);
+        qb = nqb - 1 - rem / g;
+        j = rem % g;
+    } else if (g > 1 && (units & 7) == 0) {
         const int r = (int)blockIdx.x >> 3;
         u = ((int)blockIdx.x & 7) + 8 * (r / g);
         j = r % g;
+        qb = nqb - 1 - (int)blockIdx.y;
     } else {
         u = (int)blockIdx.x / g;
         j = (int)blockIdx.x % g;
+        qb = nqb - 1 - (int)blockIdx.y;
     }
     const int b = u / Hkv, kvh = u % Hkv;
     const int bh = b * Hq + kvh * g + j;
@@ -375,8 +389,16 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t q_s[3][kBQ2 * QPAD];
     __shared__ __attribute__((aligned(16))) float lse_s[3][kBQ2];
 
-    const int kb = blockIdx.y;                      // block 0 has most rows
-    const int unit = blockIdx.x;                    // b * Hkv + kvh
+    // x = unit, y = key block (block 0 has most rows, dispatched first);
+    // with many units each XCD takes one unit's key blocks after another,
+    // so the blocks it holds at once read the same Q tiles through its L2.
+    int kb = blockIdx.y, unit = blockIdx.x;
+    if (((int)gridDim.x & 7) == 0 && (int)gridDim.x >= 64) {
+        const int L = (int)blockIdx.y * (int)gridDim.x + (int)blockIdx.x;
+        const int s = L >> 3;
+        unit = (L & 7) + 8 * (s / (int)gridDim.y);
+        kb = s % (int)gridDim.y;
+    }
     const int b = unit / Hkv, kvh = unit % Hkv;
     const int g = Hq / Hkv;
     const int tid = threadIdx.x;
