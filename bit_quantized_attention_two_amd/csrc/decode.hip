@@ -151,7 +151,13 @@ struct alignas(16) WaveLds {
 // meta are staged in LDS.  Phase V: NPASS passes over the value channels;
 // pass P covers 16-channel groups [P*GPP, (P+1)*GPP) for every head, so its
 // 16 B-operand columns are exactly the (head, group) pairs its rows need.
-template <int D, int G, bool FULLV>
+//
+// ONE: the wave holds at most 64 tokens (one key batch, two value steps).
+// Its value meta and every value word are then requested at the start,
+// together with the key loads, so the wave waits for memory once instead
+// of once per phase; this is the form for small calls, whose time is the
+// latency of that chain rather than bandwidth.
+template <int D, int G, bool FULLV, bool ONE>
 __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                                             int nt, WaveLds<D, G> &L,
                                             float *m_out, float *l_out) {
@@ -305,12 +311,73 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             for (int i = 0; i < 4; ++i) L.bias[(4 * qd + i) * G + r] = cb[i] * a.qscale;
     };
 
+    // value meta of the lane's token lane + 64 k (indices clamped)
+    constexpr int NK = ONE ? 1 : kMaxWaveChunk / 64;
+    constexpr int MW = NG16 / 2;                  // dwords of fp16 per token
+    uint32_t msr[NK][MW], mzr[NK][MW];
+    auto load_vmeta = [&](int k) {
+        const size_t row = (size_t)(t0 + min(lane + 64 * k, nt - 1)) * NGV;
+        if constexpr (FULLV && MW == 4) {
+            const uint4 xs = *reinterpret_cast<const uint4 *>(vs + row);
+            const uint4 xz = *reinterpret_cast<const uint4 *>(vz + row);
+            msr[k][0] = xs.x; msr[k][1] = xs.y; msr[k][2] = xs.z; msr[k][3] = xs.w;
+            mzr[k][0] = xz.x; mzr[k][1] = xz.y; mzr[k][2] = xz.z; mzr[k][3] = xz.w;
+        } else if constexpr (FULLV) {
+            const uint2 xs = *reinterpret_cast<const uint2 *>(vs + row);
+            const uint2 xz = *reinterpret_cast<const uint2 *>(vz + row);
+            msr[k][0] = xs.x; msr[k][1] = xs.y;
+            mzr[k][0] = xz.x; mzr[k][1] = xz.y;
+        } else {
+            // value groups of Gv > 16 channels: repeat per 16-channel part
+            const int per = NG16 / NGV;
+#pragma unroll
+            for (int j = 0; j < MW; ++j) {
+                msr[k][j] = (uint32_t)vs[row + (2 * j) / per] |
+                            ((uint32_t)vs[row + (2 * j + 1) / per] << 16);
+                mzr[k][j] = (uint32_t)vz[row + (2 * j) / per] |
+                            ((uint32_t)vz[row + (2 * j + 1) / per] << 16);
+            }
+        }
+    };
+    // value words of pass P, 32-token step st: channels P CP + r MBP + mb
+    // of the 16-token block that lane quarter qd >> 1 multiplies
+    const int last_blk = (t0 + nt) / 16 - 1;
+    auto load_vw = [&](int P, int st, uint32_t *vw) {
+        const int blk = min((t0 + st) / 16 + (qd >> 1), last_blk);
+        const uint32_t *wp = vq + (uint32_t)(blk * D + P * CP + r * MBP);
+        if constexpr (MBP == 8) {
+            const uint4 x0 = *reinterpret_cast<const uint4 *>(wp);
+            const uint4 x1 = *reinterpret_cast<const uint4 *>(wp + 4);
+            vw[0] = x0.x; vw[1] = x0.y; vw[2] = x0.z; vw[3] = x0.w;
+            vw[4] = x1.x; vw[5] = x1.y; vw[6] = x1.z; vw[7] = x1.w;
+        } else if constexpr (MBP == 4) {
+            const uint4 x0 = *reinterpret_cast<const uint4 *>(wp);
+            vw[0] = x0.x; vw[1] = x0.y; vw[2] = x0.z; vw[3] = x0.w;
+        } else if constexpr (MBP == 2) {
+            const uint2 x0 = *reinterpret_cast<const uint2 *>(wp);
+            vw[0] = x0.x; vw[1] = x0.y;
+        } else {
+            vw[0] = wp[0];
+        }
+    };
+
     // ============================================================ phase K
     load_kscale(0);
     load_kzero(0);
     __builtin_amdgcn_sched_barrier(0);
     load_kwords(0);
     __builtin_amdgcn_sched_barrier(0);
+    constexpr int NVE = ONE ? 2 : 1;              // value steps held early
+    uint32_t vwe[NPASS][NVE][MBP];
+    if constexpr (ONE) {
+        static_assert(BT == 64, "one key batch must cover the wave's tokens");
+        load_vmeta(0);
+#pragma unroll
+        for (int P = 0; P < NPASS; ++P)
+#pragma unroll
+            for (int e = 0; e < NVE; ++e) load_vw(P, 32 * e, vwe[P][e]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (G == 1) {                       // 16 groups cover the wave
         build_b();
         build_bias();
@@ -326,10 +393,12 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                 build_bias();
                 wave_lds_sync();
             }
-            __builtin_amdgcn_sched_barrier(0);
-            load_kscale(nxt);
-            load_kzero(nxt);
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!ONE) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_kscale(nxt);
+                load_kzero(nxt);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         const int gb = (tok / bblk) * NG;         // first group of the operand
 #pragma unroll
@@ -354,9 +423,11 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                 *reinterpret_cast<float4_t *>(&L.ls[hk * kLsStride + tok + 16 * j + 4 * qd]) = lg;
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        load_kwords(nxt);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!ONE) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_kwords(nxt);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // ================================================== softmax, staging
@@ -371,34 +442,9 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     const int nt32 = (nt + 31) & ~31;
     // the value meta of all of this lane's tokens (t = lane + 64 k), loads
     // issued together so that their latencies overlap
-    constexpr int NK = kMaxWaveChunk / 64;
-    constexpr int MW = NG16 / 2;                  // dwords of fp16 per token
-    uint32_t msr[NK][MW], mzr[NK][MW];
+    if constexpr (!ONE)
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-        const size_t row = (size_t)(t0 + min(lane + 64 * k, nt - 1)) * NGV;
-        if constexpr (FULLV && MW == 4) {
-            const uint4 xs = *reinterpret_cast<const uint4 *>(vs + row);
-            const uint4 xz = *reinterpret_cast<const uint4 *>(vz + row);
-            msr[k][0] = xs.x; msr[k][1] = xs.y; msr[k][2] = xs.z; msr[k][3] = xs.w;
-            mzr[k][0] = xz.x; mzr[k][1] = xz.y; mzr[k][2] = xz.z; mzr[k][3] = xz.w;
-        } else if constexpr (FULLV) {
-            const uint2 xs = *reinterpret_cast<const uint2 *>(vs + row);
-            const uint2 xz = *reinterpret_cast<const uint2 *>(vz + row);
-            msr[k][0] = xs.x; msr[k][1] = xs.y;
-            mzr[k][0] = xz.x; mzr[k][1] = xz.y;
-        } else {
-            // value groups of Gv > 16 channels: repeat per 16-channel part
-            const int per = NG16 / NGV;
-#pragma unroll
-            for (int j = 0; j < MW; ++j) {
-                msr[k][j] = (uint32_t)vs[row + (2 * j) / per] |
-                            ((uint32_t)vs[row + (2 * j + 1) / per] << 16);
-                mzr[k][j] = (uint32_t)vz[row + (2 * j) / per] |
-                            ((uint32_t)vz[row + (2 * j + 1) / per] << 16);
-            }
-        }
-    }
+        for (int k = 0; k < NK; ++k) load_vmeta(k);
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
         const int t = lane + 64 * k;
@@ -428,7 +474,6 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     // ============================================================ phase V
     // token slots of this lane in a 32-token step: tb + i, tb + 8 + i
     const int tb = 16 * (qd >> 1) + 4 * (qd & 1);
-    const int last_blk = (t0 + nt) / 16 - 1;
     float4_t outv[NPASS][MBP];                    // kept columns, see below
     float zsum[NPASS];
 #pragma unroll
@@ -440,34 +485,25 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
 #pragma unroll
         for (int mb = 0; mb < MBP; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
         float za[4] = {0.f, 0.f, 0.f, 0.f};
-        // value words: channels P CP + r MBP + mb of a 16-token block
         uint32_t vw[MBP];
-        auto load_vw = [&](int st) {
-            const int blk = min((t0 + st) / 16 + (qd >> 1), last_blk);
-            const uint32_t *wp = vq + (uint32_t)(blk * D + P * CP + r * MBP);
-            if constexpr (MBP == 8) {
-                const uint4 x0 = *reinterpret_cast<const uint4 *>(wp);
-                const uint4 x1 = *reinterpret_cast<const uint4 *>(wp + 4);
-                vw[0] = x0.x; vw[1] = x0.y; vw[2] = x0.z; vw[3] = x0.w;
-                vw[4] = x1.x; vw[5] = x1.y; vw[6] = x1.z; vw[7] = x1.w;
-            } else if constexpr (MBP == 4) {
-                const uint4 x0 = *reinterpret_cast<const uint4 *>(wp);
-                vw[0] = x0.x; vw[1] = x0.y; vw[2] = x0.z; vw[3] = x0.w;
-            } else if constexpr (MBP == 2) {
-                const uint2 x0 = *reinterpret_cast<const uint2 *>(wp);
-                vw[0] = x0.x; vw[1] = x0.y;
-            } else {
-                vw[0] = wp[0];
-            }
-        };
-        load_vw(0);
-        for (int st = 0; st < nt32; st += 32) {
+        if constexpr (!ONE) load_vw(P, 0, vw);
+        const int nsteps = nt32 >> 5;
+#pragma unroll(ONE ? NVE : 1)
+        for (int e = 0; e < (ONE ? NVE : nsteps); ++e) {
+            if (ONE && e >= nsteps) break;        // uniform
+            const int st = 32 * e;
             half8_t av[MBP];
+            if constexpr (ONE) {
 #pragma unroll
-            for (int mb = 0; mb < MBP; ++mb) av[mb] = code_operand(vw[mb] >> (8 * (qd & 1)));
-            __builtin_amdgcn_sched_barrier(0);
-            load_vw(min(st + 32, nt32 - 32));
-            __builtin_amdgcn_sched_barrier(0);
+                for (int mb = 0; mb < MBP; ++mb)
+                    av[mb] = code_operand(vwe[P][e][mb] >> (8 * (qd & 1)));
+            } else {
+#pragma unroll
+                for (int mb = 0; mb < MBP; ++mb) av[mb] = code_operand(vw[mb] >> (8 * (qd & 1)));
+                __builtin_amdgcn_sched_barrier(0);
+                load_vw(P, min(st + 32, nt32 - 32), vw);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             const float *pp = &L.ls[hc * kLsStride + st + tb];
             const half_t *sp = &L.sv[vg * kSvStride + st + tb];
             const half_t *zp = &L.zv[vg * kSvStride + st + tb];
@@ -661,7 +697,7 @@ __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0
 }
 
 // FULLV: value channel groups of 16 (D/16 scales per token).
-template <int D, int G, bool FULLV>
+template <int D, int G, bool FULLV, bool ONE>
 __global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_kernel(DecArgs a) {
     // x = unit, y = split: with the round-robin dispatch of workgroups over
     // the 8 XCDs, every split of a unit (and its merge below) runs on the
@@ -687,7 +723,7 @@ __global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_k
         const int wchunk = a.chunk / kWaves;
         const int t0 = split * a.chunk + wave * wchunk;
         const int nt = max(0, min(wchunk, a.n_packed - t0));
-        if (nt > 0) packed_wave<D, G, FULLV>(a, unit, t0, nt, lds[wave], m_w, l_w);
+        if (nt > 0) packed_wave<D, G, FULLV, ONE>(a, unit, t0, nt, lds[wave], m_w, l_w);
     } else {
         const int per = (a.n_res + kWaves - 1) / kWaves;
         const int t0 = wave * per;
@@ -828,10 +864,17 @@ int pick_chunk(int units, int n_packed, int Gk, int g) {
 
 template <int D, int G>
 hipError_t launch_decode_dg(const DecArgs &a, int units, hipStream_t stream) {
-    if (a.c.Gv == 16)
-        decode_kernel<D, G, true><<<dim3(units, a.nsplit), kThreads, 0, stream>>>(a);
-    else
-        decode_kernel<D, G, false><<<dim3(units, a.nsplit), kThreads, 0, stream>>>(a);
+    // one key batch per wave (64-token wave shares): the early-load form,
+    // for g <= 2 (at g = 4 its registers would spill)
+    const bool one = G <= 2 && a.chunk == kMinWaveChunk * kWaves;
+    const dim3 grid(units, a.nsplit);
+    if (a.c.Gv == 16) {
+        if (one) decode_kernel<D, G, true, G <= 2><<<grid, kThreads, 0, stream>>>(a);
+        else decode_kernel<D, G, true, false><<<grid, kThreads, 0, stream>>>(a);
+    } else {
+        if (one) decode_kernel<D, G, false, G <= 2><<<grid, kThreads, 0, stream>>>(a);
+        else decode_kernel<D, G, false, false><<<grid, kThreads, 0, stream>>>(a);
+    }
     decode_combine_kernel<D, G><<<dim3(units, G), kThreads, 0, stream>>>(
         a.part_ml, a.part_o, a.nsplit, a.o);
     return hipGetLastError();
