@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--eager", action="store_true",
                    help="launch every call from Python instead of replaying "
                         "the captured HIP graphs of a step")
+    p.add_argument("--no-large-decode", action="store_true",
+                   help="skip the decode-call timing at the 13B-shaped "
+                        "batched layer (16 x 40 kv heads, 4096 packed tokens)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="rough CPU budget of the oracle baseline")
     p.add_argument("--traffic-probe", action="store_true",
@@ -129,6 +132,73 @@ def traffic_probe():
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": src.numel() * 4, "decode_calls": L,
                       "algorithmic_bytes_per_call": alg / L}), flush=True)
+
+
+def large_decode_roofline(stream):
+    """Decode-attention call at the Llama2-13B-shaped batched layer (batch
+    16, 40 heads, D 128, Gk = Gv = 16): 4096 selected tokens packed plus 64
+    residual tokens per kv head, the state halfway through its decode steps.
+    One call moves ~360 MB, so this is the call in its bandwidth regime; the
+    bench workload's 4096-token layer (~9 MB per call) is latency-bound.
+    Two such caches alternate (720 MB, more than the 256 MB last-level
+    cache, so no call finds the previous call's data there), timed as a
+    graph of back-to-back calls between HIP events on `stream`; the median
+    of 5 replays is reported."""
+    import torch
+    from bit_quantized_attention_two_amd import configs, minikv
+    c = configs.get(3)
+    B, Hq, Hkv, D, n = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"]
+    dims = minikv.make_dims(B, Hq, Hkv, D, c["Gk"], c["Gv"], c["residual_cap"])
+    m, res = 4096, 64
+    g = torch.Generator(device="cuda").manual_seed(3)
+    k = torch.randn(B, Hkv, n, D, device="cuda", generator=g).half()
+    v = torch.randn(B, Hkv, n, D, device="cuda", generator=g).half()
+    sel = (torch.arange(m, device="cuda", dtype=torch.int64) * n // m
+           ).int().repeat(B, Hkv, 1).contiguous()
+    caches = []
+    for i in range(2):
+        cache = minikv.LayerCache(dims, m + 256)
+        minikv.pack(dims, k, v, (sel + i) % n, cache)
+        for t in range(res):                     # 64 decode-step tokens
+            minikv.append(dims, cache, k[:, :, t].contiguous(),
+                          v[:, :, t].contiguous())
+        assert cache.n_packed == m and cache.n_res == res
+        caches.append(cache)
+    del k, v
+    q = torch.randn(B, Hq, D, device="cuda", generator=g).half()
+    o = torch.empty_like(q)
+    ws = torch.zeros(minikv.decode_ws_bytes(dims, caches[0].capacity),
+                     dtype=torch.uint8, device="cuda")
+    R = 20
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        minikv.decode_attn(dims, caches[0], q, o=o, ws=ws)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=side):
+            for i in range(R):
+                minikv.decode_attn(dims, caches[i % 2], q, o=o, ws=ws)
+    stream.wait_stream(side)
+    gr.replay()
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for a, b in ev:
+        a.record(stream)
+        gr.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 / R
+    alg = decode_bytes(c, m, res)
+    achieved = alg / (us * 1e-6) / 1e9
+    return {"kernel": "minikv_decode_attn (split-KV decode + combine "
+                      "kernels)",
+            "workload": "llama2-13b-8k batched decode layer: batch 16, 40 "
+                        "kv heads, D 128, 4096 packed + 64 residual tokens",
+            "bound": "hbm", "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(us, 3),
+            "algorithmic_bytes_per_launch": int(alg), "launches": R}
 
 
 def decode_bytes(c, n_packed, n_res):
@@ -371,6 +441,10 @@ def main():
         },
         "input_generation_s": round(gen_s, 1),
     }
+    if not args.no_large_decode:
+        del qkv, outs, cols, graphs, g_kern
+        torch.cuda.empty_cache()
+        result["roofline_decode_large"] = large_decode_roofline(stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, c, ks, r, args.cpu_seconds)
     print(json.dumps(result), flush=True)
