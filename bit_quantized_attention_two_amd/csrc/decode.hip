@@ -474,24 +474,35 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     // ============================================================ phase V
     // token slots of this lane in a 32-token step: tb + i, tb + 8 + i
     const int tb = 16 * (qd >> 1) + 4 * (qd & 1);
+    // Column r of pass P is (head r / GPP, group P GPP + r % GPP): the head
+    // does not depend on the pass, so every pass of a step shares the
+    // lane's probabilities, and the passes run inside one walk over the
+    // steps (one chain of dependent value loads, not NPASS of them).
+    const int hc = min(r / GPP, G - 1);
     float4_t outv[NPASS][MBP];                    // kept columns, see below
-    float zsum[NPASS];
+    float za[NPASS][4];
 #pragma unroll
     for (int P = 0; P < NPASS; ++P) {
-        // column r of this pass = (head r / GPP, group P GPP + r % GPP)
-        const int hc = min(r / GPP, G - 1);
-        const int vg = P * GPP + r % GPP;
-        float4_t acc[MBP];
 #pragma unroll
-        for (int mb = 0; mb < MBP; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
-        float za[4] = {0.f, 0.f, 0.f, 0.f};
-        uint32_t vw[MBP];
-        if constexpr (!ONE) load_vw(P, 0, vw);
-        const int nsteps = nt32 >> 5;
+        for (int mb = 0; mb < MBP; ++mb) outv[P][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) za[P][i] = 0.f;
+    }
+    uint32_t vw[NPASS][MBP];
+    if constexpr (!ONE)
+#pragma unroll
+        for (int P = 0; P < NPASS; ++P) load_vw(P, 0, vw[P]);
+    const int nsteps = nt32 >> 5;
 #pragma unroll(ONE ? NVE : 1)
-        for (int e = 0; e < (ONE ? NVE : nsteps); ++e) {
-            if (ONE && e >= nsteps) break;        // uniform
-            const int st = 32 * e;
+    for (int e = 0; e < (ONE ? NVE : nsteps); ++e) {
+        if (ONE && e >= nsteps) break;            // uniform
+        const int st = 32 * e;
+        const float *pp = &L.ls[hc * kLsStride + st + tb];
+        const float4_t p0 = *reinterpret_cast<const float4_t *>(pp);
+        const float4_t p1 = *reinterpret_cast<const float4_t *>(pp + 8);
+#pragma unroll
+        for (int P = 0; P < NPASS; ++P) {
+            const int vg = P * GPP + r % GPP;
             half8_t av[MBP];
             if constexpr (ONE) {
 #pragma unroll
@@ -499,16 +510,13 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                     av[mb] = code_operand(vwe[P][e][mb] >> (8 * (qd & 1)));
             } else {
 #pragma unroll
-                for (int mb = 0; mb < MBP; ++mb) av[mb] = code_operand(vw[mb] >> (8 * (qd & 1)));
+                for (int mb = 0; mb < MBP; ++mb) av[mb] = code_operand(vw[P][mb] >> (8 * (qd & 1)));
                 __builtin_amdgcn_sched_barrier(0);
-                load_vw(P, min(st + 32, nt32 - 32), vw);
+                load_vw(P, min(st + 32, nt32 - 32), vw[P]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            const float *pp = &L.ls[hc * kLsStride + st + tb];
             const half_t *sp = &L.sv[vg * kSvStride + st + tb];
             const half_t *zp = &L.zv[vg * kSvStride + st + tb];
-            const float4_t p0 = *reinterpret_cast<const float4_t *>(pp);
-            const float4_t p1 = *reinterpret_cast<const float4_t *>(pp + 8);
             const half4_t s0 = *reinterpret_cast<const half4_t *>(sp);
             const half4_t s1 = *reinterpret_cast<const half4_t *>(sp + 8);
             const half4_t z0 = *reinterpret_cast<const half4_t *>(zp);
@@ -522,23 +530,25 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                 bhw[i] = hw;
                 blw[i] = lw;
                 // p is stored times 4^-i: keep one z sum per i
-                za[i] = __builtin_fmaf(p0[i], (float)z0[i], za[i]);
-                za[i] = __builtin_fmaf(p1[i], (float)z1[i], za[i]);
+                za[P][i] = __builtin_fmaf(p0[i], (float)z0[i], za[P][i]);
+                za[P][i] = __builtin_fmaf(p1[i], (float)z1[i], za[P][i]);
             }
             const half8_t bh = __builtin_bit_cast(half8_t, bhw);
             const half8_t bl = __builtin_bit_cast(half8_t, blw);
 #pragma unroll
             for (int mb = 0; mb < MBP; ++mb) {
-                acc[mb] = mfma16(av[mb], bh, acc[mb]);
-                acc[mb] = mfma16(av[mb], bl, acc[mb]);
+                outv[P][mb] = mfma16(av[mb], bh, outv[P][mb]);
+                outv[P][mb] = mfma16(av[mb], bl, outv[P][mb]);
             }
         }
-        float zt = za[0] + __builtin_amdgcn_ldexpf(za[1], 2) +
-                   __builtin_amdgcn_ldexpf(za[2], 4) + __builtin_amdgcn_ldexpf(za[3], 6);
+    }
+    float zsum[NPASS];
+#pragma unroll
+    for (int P = 0; P < NPASS; ++P) {
+        float zt = za[P][0] + __builtin_amdgcn_ldexpf(za[P][1], 2) +
+                   __builtin_amdgcn_ldexpf(za[P][2], 4) + __builtin_amdgcn_ldexpf(za[P][3], 6);
         zt += shfl_xor(zt, 16);
         zt += shfl_xor(zt, 32);
-#pragma unroll
-        for (int mb = 0; mb < MBP; ++mb) outv[P][mb] = acc[mb];
         zsum[P] = zt;
     }
     wave_lds_sync();
