@@ -182,6 +182,27 @@ def test_decode_full_size(cfg_id):
     _decode_and_compare(torch, mk, dims, cache, oc, q, units)
 
 
+@pytest.mark.parametrize("D,g,Gv", [(128, 1, 16), (128, 2, 16), (64, 2, 32),
+                                    (128, 1, 64)])
+def test_decode_multi_batch_waves(D, g, Gv):
+    """Enough units (8 x 32 kv heads) that the split size grows past the
+    minimum: each wave then walks several 64-token key batches and many
+    value steps, the form the small tests (4 units, single-batch waves)
+    never reach for g <= 2.  16 sampled units against the oracle."""
+    torch, mk = require_gpu()
+    B, Hkv, n, m = 8, 32, 2200, 2100
+    say("decode-multibatch", dict(D=D, g=g, Gv=Gv))
+    units = [(b, h) for b in range(B) for h in range(Hkv)]
+    rr = np.random.default_rng(D + g + Gv)
+    units = [units[i] for i in sorted(rr.choice(len(units), 16, replace=False))]
+    dims, cache, oc = _build(torch, mk, B, Hkv, g, D, 16, Gv, n, m,
+                             seed=40 + g + Gv, check_bits=False, units=units)
+    q, kn, vn = synth.gen_decode_step(7, 0, 0, B, Hkv * g, Hkv, D)
+    mk.append(dims, cache, dev16(torch, kn), dev16(torch, vn))
+    oc.append(kn, vn)
+    _decode_and_compare(torch, mk, dims, cache, oc, q, units)
+
+
 @pytest.mark.parametrize("g,D", [(1, 128), (4, 128), (2, 64)])
 def test_append_decode_equals_separate_calls(g, D):
     """The fused entry point gives the same bits as minikv_append followed by
