@@ -41,7 +41,7 @@ def _load():
         lib.oracle_pack_unit.argtypes = [i32, i32, i32, P, P, P, i32] + [P] * 8
         lib.oracle_pack_unit.restype = i32
         lib.oracle_decode_unit.argtypes = [i32, i32, i32, i32, P, i32] + \
-            [P] * 6 + [i32, P, P, P]
+            [P] * 6 + [i32, P, P, P, P]
         lib.oracle_decode_unit.restype = i32
         lib.oracle_cache_bytes.argtypes = [i32, i32, i32, i32, i32,
                                            ctypes.c_double, i32, i32, P]
@@ -172,20 +172,24 @@ def pack_unit(k, v, sel, Gk, Gv):
 # ------------------------------------------------------------------ decode --
 
 def decode_unit(q, Gk, Gv, n_packed, kq, ks, kz, vq, vs, vz, n_res, kres,
-                vres):
+                vres, with_mass=False):
     """q [g][D]; packed arrays of one unit (first n_packed tokens used);
-    kres/vres [>=n_res][D].  Returns o [g][D] fp64."""
+    kres/vres [>=n_res][D].  Returns o [g][D] fp64, and with_mass also the
+    attention weight of every cached token summed over the g heads,
+    [n_packed + n_res] fp64 in cache order."""
     q = _u16(q)
     g, D = q.shape
     arrs = [np.ascontiguousarray(a) for a in (kq, ks, kz, vq, vs, vz)]
     kres, vres = _u16(kres), _u16(vres)
     o = np.zeros((g, D), np.float64)
+    mass = np.zeros(max(n_packed + n_res, 1), np.float64) if with_mass else None
     rc = _load().oracle_decode_unit(D, g, Gk, Gv, _ptr(q), n_packed,
                                     *[_ptr(a) for a in arrs], n_res,
-                                    _ptr(kres), _ptr(vres), _ptr(o))
+                                    _ptr(kres), _ptr(vres), _ptr(o),
+                                    _ptr(mass) if with_mass else None)
     if rc != 0:
         raise ValueError("bad decode arguments")
-    return o
+    return (o, mass[:n_packed + n_res]) if with_mass else o
 
 
 # -------------------------------------------------------------- cache size --
@@ -300,8 +304,9 @@ class OracleCache:
                                                        b, h)
         return o
 
-    def decode_unit(self, qg, b, h):
+    def decode_unit(self, qg, b, h, with_mass=False):
         return decode_unit(qg, self.Gk, self.Gv, self.n_packed,
                            self.kq[b, h], self.ks[b, h], self.kz[b, h],
                            self.vq[b, h], self.vs[b, h], self.vz[b, h],
-                           self.n_res, self.kres[b, h], self.vres[b, h])
+                           self.n_res, self.kres[b, h], self.vres[b, h],
+                           with_mass)

@@ -422,13 +422,21 @@ int oracle_pack_unit(int D, int Gk, int Gv, const uint16_t *k,
 /*   q [g][D] fp16; cache arrays as oracle_pack_unit writes them with       */
 /*   n_packed tokens (multiple of Gk); kres, vres [n_res][D] fp16;          */
 /*   o [g][D] fp64.                                                         */
+/*                                                                          */
+/* mass (nullable) [n_packed + n_res] fp64: the attention weight of every   */
+/*   cached token, summed over the g query heads, in cache order (packed    */
+/*   tokens, then residual slots).  [V] referee_report.major_comments[0]    */
+/*   and the verdict's falsifier field: whether the heavy hitters chosen at */
+/*   the end of prefill stay the tokens decoding attends to is measured by  */
+/*   this per-step attention mass.                                          */
 /* ------------------------------------------------------------------------ */
 
 int oracle_decode_unit(int D, int g, int Gk, int Gv, const uint16_t *q,
                        int n_packed, const uint32_t *kq, const uint16_t *ks,
                        const uint16_t *kz, const uint32_t *vq,
                        const uint16_t *vs, const uint16_t *vz, int n_res,
-                       const uint16_t *kres, const uint16_t *vres, double *o)
+                       const uint16_t *kres, const uint16_t *vres, double *o,
+                       double *mass)
 {
     int T = n_packed + n_res;
     if (T <= 0 || n_packed % Gk || D % 16 || D % Gv)
@@ -466,6 +474,12 @@ int oracle_decode_unit(int D, int g, int Gk, int Gv, const uint16_t *q,
         for (int t = 0; t < T; ++t) {
             s[t] = exp(s[t] - M);
             l += s[t];
+        }
+        if (mass) {
+            for (int t = 0; t < T; ++t) {
+                if (h == 0) mass[t] = 0.0;
+                mass[t] += s[t] / l;
+            }
         }
         for (int c = 0; c < D; ++c) {
             double acc = 0.0;

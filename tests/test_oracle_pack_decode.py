@@ -178,3 +178,33 @@ def test_decode_vs_sdpa_over_independent_dequant(oracle, Gk, g):
                              out["vq"], out["vs"], out["vz"], m - mp,
                              out["kres"], out["vres"])
     assert np.all(os_ == os_[:1])
+
+
+@pytest.mark.parametrize("Gk,g", [(16, 1), (16, 4), (32, 2)])
+def test_decode_mass_is_the_attention_weights(oracle, Gk, g):
+    """The per-token decode mass (the persistence audit's measurement) is
+    the softmax weight of each cached token summed over the g heads: checked
+    against torch softmax over an independent unpacking of the same cache,
+    Σ mass = g, uniform g/T for q = 0, and o unchanged by asking for it."""
+    n, D, Gv, m = 300, 64, 16, 170
+    k, v = synth.gen_kv(12, 1, n, D)
+    sel = synth.gen_selection(13, 1, n, m)[0]
+    out = oracle.pack_unit(k[0], v[0], sel, Gk, Gv)
+    mp = (m // Gk) * Gk
+    args = (Gk, Gv, mp, out["kq"], out["ks"], out["kz"], out["vq"],
+            out["vs"], out["vz"], m - mp, out["kres"], out["vres"])
+    r = np.random.default_rng(3)
+    q = (r.standard_normal((g, D)) * 0.5).astype(np.float16)
+    o, mass = oracle.decode_unit(q, *args, with_mass=True)
+    assert mass.shape == (m,)
+    assert np.array_equal(o, oracle.decode_unit(q, *args))
+    K = np.concatenate([_unpack_keys(out["kq"], out["ks"], out["kz"], mp, Gk),
+                        out["kres"].view(np.float16).astype(np.float32)])
+    logits = torch.from_numpy(q.astype(np.float64)) @ \
+        torch.from_numpy(K.astype(np.float64)).T / np.sqrt(D)
+    ref = torch.softmax(logits, dim=-1).sum(0).numpy()
+    np.testing.assert_allclose(mass, ref, rtol=1e-11, atol=1e-14)
+    assert abs(mass.sum() - g) < 1e-12
+    _, m0 = oracle.decode_unit(np.zeros((g, D), np.float16), *args,
+                               with_mass=True)
+    np.testing.assert_allclose(m0, np.full(m, g / m), rtol=1e-12)
