@@ -360,6 +360,23 @@ def main():
     kb.record(stream)
     torch.cuda.synchronize()
     dec_call_ms = np.array([ka.elapsed_time(kb) / (R * L)])
+    # the same calls with the persistence audit's per-token mass output
+    mass = torch.zeros((B, Hkv, max_cap + nr), dtype=torch.float32,
+                       device=dev)
+    ws_mass = torch.empty(minikv.decode_mass_ws_bytes(dims, max_cap),
+                          dtype=torch.uint8, device=dev)
+    side.wait_stream(stream)
+    g_mass = capture(lambda: [minikv.decode_attn_mass(dims, caches[l],
+                                                      dq[0, l % nl], mass,
+                                                      o=od, ws=ws_mass)
+                              for _ in range(R) for l in range(L)], side)
+    stream.wait_stream(side)
+    g_mass.replay()
+    ka.record(stream)
+    g_mass.replay()
+    kb.record(stream)
+    torch.cuda.synchronize()
+    mass_call_ms = ka.elapsed_time(kb) / (R * L)
     dec_call_bytes = np.array([decode_bytes(c, x.n_packed, x.n_res)
                                for x in caches], np.float64)
     pre_call_ms = []
@@ -439,10 +456,16 @@ def main():
             "avg_launch_us": round(float(pre_call_ms.mean()) * 1e3, 3),
             "algorithmic_flops_per_launch": prefill_flops(c),
         },
+        "decode_mass_audit": {
+            "kernel": "minikv_decode_attn_mass (decode + per-token "
+                      "attention mass, accumulated)",
+            "avg_launch_us": round(mass_call_ms * 1e3, 3),
+            "vs_decode_call": round(mass_call_ms / avg_dec_ms, 3),
+        },
         "input_generation_s": round(gen_s, 1),
     }
     if not args.no_large_decode:
-        del qkv, outs, cols, graphs, g_kern
+        del qkv, outs, cols, graphs, g_kern, g_mass
         torch.cuda.empty_cache()
         result["roofline_decode_large"] = large_decode_roofline(stream)
     if not args.no_cpu_baseline:

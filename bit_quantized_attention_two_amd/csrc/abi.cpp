@@ -258,6 +258,17 @@ int32_t minikv_decode_ws_bytes(const minikv_dims *d, int32_t capacity,
     return ok();
 }
 
+int32_t minikv_decode_mass_ws_bytes(const minikv_dims *d, int32_t capacity,
+                                    size_t *out) {
+    CHECK(check_dims(d));
+    if (!out) return fail(MINIKV_EINVAL, "out is NULL");
+    if (capacity < 0) return fail(MINIKV_EINVAL, "capacity < 0");
+    *out = minikv::decode_mass_ws_bytes(d->batch * d->n_kv_heads,
+                                        d->n_q_heads / d->n_kv_heads, d->head_dim,
+                                        capacity, d->residual_cap);
+    return ok();
+}
+
 int32_t minikv_prefill_attn(const minikv_dims *d, int32_t n, const void *q,
                             const void *k, const void *v, void *o, float *lse,
                             float *col, void *stream) {
@@ -477,6 +488,34 @@ int32_t minikv_append_decode(const minikv_dims *d, minikv_layer_cache *c,
         "append+decode launch");
     if (st == MINIKV_OK) c->n_res += 1;
     return st;
+}
+
+int32_t minikv_decode_attn_mass(const minikv_dims *d, const minikv_layer_cache *c,
+                                const void *q, void *o, float *mass,
+                                int32_t mass_stride, void *ws, size_t ws_bytes,
+                                void *stream) {
+    CHECK(check_dims(d));
+    CHECK(check_cache(d, c));
+    CHECK(check_decode(d, c, q, o, ws, ws_bytes));
+    CHECK_PTR(mass, "mass");
+    if (c->n_packed + c->n_res == 0) return fail(MINIKV_EINVAL, "cache holds no token");
+    if (mass_stride < c->n_packed + c->n_res)
+        return fail(MINIKV_EINVAL, "mass_stride %d < %d cached tokens", mass_stride,
+                    c->n_packed + c->n_res);
+    const int units = d->batch * d->n_kv_heads;
+    const int g = d->n_q_heads / d->n_kv_heads;
+    const size_t need = minikv::decode_mass_ws_bytes(units, g, d->head_dim, c->capacity,
+                                                     d->residual_cap);
+    if (ws_bytes < need)
+        return fail(MINIKV_EINVAL, "workspace too small: %zu < %zu", ws_bytes, need);
+    CHECK(check_device());
+    const minikv::MassOut mo{mass, mass_stride};
+    return hip_status(minikv::launch_decode(static_cast<const uint16_t *>(q),
+                                            static_cast<uint16_t *>(o), units, g,
+                                            c->n_packed, c->n_res, view_of(d, c),
+                                            nullptr, nullptr, ws, ws_bytes,
+                                            static_cast<hipStream_t>(stream), &mo),
+                      "decode+mass launch");
 }
 
 }  // extern "C"

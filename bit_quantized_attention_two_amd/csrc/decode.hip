@@ -63,6 +63,8 @@ struct DecArgs {
     int new_slot;                    // residual slot of the new token
     float *part_ml;                  // [units][nsplit][G][2]
     float *part_o;                   // [units][nsplit][G][D]
+    float *lg;                       // nullable: logits out, log2 units,
+    int lg_stride;                   //   [units][G][lg_stride], cache order
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -157,7 +159,7 @@ struct alignas(16) WaveLds {
 // together with the key loads, so the wave waits for memory once instead
 // of once per phase; this is the form for small calls, whose time is the
 // latency of that chain rather than bandwidth.
-template <int D, int G, bool FULLV, bool ONE>
+template <int D, int G, bool FULLV, bool ONE, bool MASS>
 __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                                             int nt, WaveLds<D, G> &L,
                                             float *m_out, float *l_out) {
@@ -421,6 +423,10 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                     mloc = fmaxf(mloc, lg[i]);
                 }
                 *reinterpret_cast<float4_t *>(&L.ls[hk * kLsStride + tok + 16 * j + 4 * qd]) = lg;
+                if constexpr (MASS)               // the mass audit's logits
+                    *reinterpret_cast<float4_t *>(
+                        a.lg + ((size_t)unit * G + hk) * a.lg_stride + t0 + tok + 16 * j +
+                        4 * qd) = lg;
             }
         }
         if constexpr (!ONE) {
@@ -581,7 +587,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
 // per token (D/16 channels each), four tokens per pass; P.V: the same lanes
 // over the same passes, the four token phases summed at the end.  The loads
 // of a batch of passes are all issued before their first use.
-template <int D, int G>
+template <int D, int G, bool MASS>
 __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0,
                                               int nt, WaveLds<D, G> &L,
                                               float *m_out, float *l_out) {
@@ -635,7 +641,11 @@ __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0
                 s = row16_sum(s) * a.qscale;
                 if (t < nt) {
                     mloc[h] = fmaxf(mloc[h], s);
-                    if (part == 0) L.ls[h * kLsStride + t] = s;
+                    if (part == 0) {
+                        L.ls[h * kLsStride + t] = s;
+                        if constexpr (MASS)       // the mass audit's logits
+                            a.lg[((size_t)unit * G + h) * a.lg_stride + a.n_packed + t0 + t] = s;
+                    }
                 }
             }
         }
@@ -707,7 +717,8 @@ __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0
 }
 
 // FULLV: value channel groups of 16 (D/16 scales per token).
-template <int D, int G, bool FULLV, bool ONE>
+// MASS: also store every token's logit for the persistence audit.
+template <int D, int G, bool FULLV, bool ONE, bool MASS>
 __global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_kernel(DecArgs a) {
     // x = unit, y = split: with the round-robin dispatch of workgroups over
     // the 8 XCDs, every split of a unit (and its merge below) runs on the
@@ -733,12 +744,12 @@ __global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_k
         const int wchunk = a.chunk / kWaves;
         const int t0 = split * a.chunk + wave * wchunk;
         const int nt = max(0, min(wchunk, a.n_packed - t0));
-        if (nt > 0) packed_wave<D, G, FULLV, ONE>(a, unit, t0, nt, lds[wave], m_w, l_w);
+        if (nt > 0) packed_wave<D, G, FULLV, ONE, MASS>(a, unit, t0, nt, lds[wave], m_w, l_w);
     } else {
         const int per = (a.n_res + kWaves - 1) / kWaves;
         const int t0 = wave * per;
         const int nt = max(0, min(per, a.n_res - t0));
-        if (nt > 0) residual_wave<D, G>(a, unit, t0, nt, lds[wave], m_w, l_w);
+        if (nt > 0) residual_wave<D, G, MASS>(a, unit, t0, nt, lds[wave], m_w, l_w);
         // store the new token into its residual slot for later calls
         if (a.k_new && wave == 0 && lane < 2 * (D / 8)) {
             const int part = lane % (D / 8);
@@ -795,7 +806,7 @@ __global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_k
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     const float *__restrict__ part_ml, const float *__restrict__ part_o,
-    int nsplit, uint16_t *__restrict__ o) {
+    int nsplit, uint16_t *__restrict__ o, float *__restrict__ ml_out) {
     constexpr int SLICES = kThreads / D;
     constexpr int NB = 8;
     __shared__ float r_m[kThreads], r_l[kThreads], r_o[kThreads];
@@ -850,7 +861,33 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
             }
         }
         o[((size_t)unit * G + h) * D + ch] = f2h_bits(acc / L);
+        if (ml_out && ch == 0) {          // the mass audit's normaliser
+            ml_out[((size_t)unit * G + h) * 2 + 0] = M;
+            ml_out[((size_t)unit * G + h) * 2 + 1] = L;
+        }
     }
+}
+
+// Persistence audit: mass[unit][t] += sum over the unit's g heads of the
+// attention weight 2^(logit - M) / L of cache token t, with the logits the
+// decode kernels stored and each head's final (M, L) from the combine.
+// One thread per token; every token is written once, so it is
+// deterministic.
+template <int G>
+__global__ __launch_bounds__(kThreads) void decode_mass_kernel(
+    const float *__restrict__ lg, int lg_stride, const float *__restrict__ ml,
+    int n_tok, float *__restrict__ mass, int mass_stride) {
+    const int unit = blockIdx.x;
+    const int t = blockIdx.y * kThreads + threadIdx.x;
+    if (t >= n_tok) return;
+    float w = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float M = ml[((size_t)unit * G + h) * 2 + 0];
+        const float L = ml[((size_t)unit * G + h) * 2 + 1];
+        w += __builtin_amdgcn_exp2f(lg[((size_t)unit * G + h) * lg_stride + t] - M) / L;
+    }
+    mass[(size_t)unit * mass_stride + t] += w;
 }
 
 // Largest chunk whose blocks still fill half of the resident block slots
@@ -873,30 +910,46 @@ int pick_chunk(int units, int n_packed, int Gk, int g) {
 }
 
 template <int D, int G>
-hipError_t launch_decode_dg(const DecArgs &a, int units, hipStream_t stream) {
+hipError_t launch_decode_dg(const DecArgs &a, int units, float *ml_out,
+                            const MassOut *mo, hipStream_t stream) {
     // one key batch per wave (64-token wave shares): the early-load form,
     // for g <= 2 (at g = 4 its registers would spill)
     const bool one = G <= 2 && a.chunk == kMinWaveChunk * kWaves;
     const dim3 grid(units, a.nsplit);
-    if (a.c.Gv == 16) {
-        if (one) decode_kernel<D, G, true, G <= 2><<<grid, kThreads, 0, stream>>>(a);
-        else decode_kernel<D, G, true, false><<<grid, kThreads, 0, stream>>>(a);
+    if (mo) {
+        if (a.c.Gv == 16) {
+            if (one) decode_kernel<D, G, true, G <= 2, true><<<grid, kThreads, 0, stream>>>(a);
+            else decode_kernel<D, G, true, false, true><<<grid, kThreads, 0, stream>>>(a);
+        } else {
+            if (one) decode_kernel<D, G, false, G <= 2, true><<<grid, kThreads, 0, stream>>>(a);
+            else decode_kernel<D, G, false, false, true><<<grid, kThreads, 0, stream>>>(a);
+        }
+    } else if (a.c.Gv == 16) {
+        if (one) decode_kernel<D, G, true, G <= 2, false><<<grid, kThreads, 0, stream>>>(a);
+        else decode_kernel<D, G, true, false, false><<<grid, kThreads, 0, stream>>>(a);
     } else {
-        if (one) decode_kernel<D, G, false, G <= 2><<<grid, kThreads, 0, stream>>>(a);
-        else decode_kernel<D, G, false, false><<<grid, kThreads, 0, stream>>>(a);
+        if (one) decode_kernel<D, G, false, G <= 2, false><<<grid, kThreads, 0, stream>>>(a);
+        else decode_kernel<D, G, false, false, false><<<grid, kThreads, 0, stream>>>(a);
     }
     decode_combine_kernel<D, G><<<dim3(units, G), kThreads, 0, stream>>>(
-        a.part_ml, a.part_o, a.nsplit, a.o);
+        a.part_ml, a.part_o, a.nsplit, a.o, ml_out);
+    if (mo) {
+        const int n_tok = a.n_packed + a.n_res;
+        decode_mass_kernel<G><<<dim3(units, (n_tok + kThreads - 1) / kThreads), kThreads, 0,
+                                stream>>>(a.lg, a.lg_stride, ml_out, n_tok, mo->mass,
+                                          mo->stride);
+    }
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_decode_d(const DecArgs &a, int units, int g, hipStream_t stream) {
+hipError_t launch_decode_d(const DecArgs &a, int units, int g, float *ml_out,
+                           const MassOut *mo, hipStream_t stream) {
     switch (g) {
-    case 1: return launch_decode_dg<D, 1>(a, units, stream);
-    case 2: return launch_decode_dg<D, 2>(a, units, stream);
-    case 4: return launch_decode_dg<D, 4>(a, units, stream);
-    case 8: return launch_decode_dg<D, 8>(a, units, stream);
+    case 1: return launch_decode_dg<D, 1>(a, units, ml_out, mo, stream);
+    case 2: return launch_decode_dg<D, 2>(a, units, ml_out, mo, stream);
+    case 4: return launch_decode_dg<D, 4>(a, units, ml_out, mo, stream);
+    case 8: return launch_decode_dg<D, 8>(a, units, ml_out, mo, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -913,6 +966,18 @@ size_t decode_ws_bytes(int units, int g, int D, int capacity) {
     return part_bytes(units, g, D, nsplit);
 }
 
+// Mass-audit workspace: the decode partials, then the logits
+// [units][g][lg_stride] and the final (M, L) [units][g][2], each region
+// 256-byte aligned.
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static int lg_stride_of(int capacity, int nr) { return (capacity + nr + 3) & ~3; }
+
+size_t decode_mass_ws_bytes(int units, int g, int D, int capacity, int nr) {
+    return align256(decode_ws_bytes(units, g, D, capacity)) +
+           align256((size_t)units * g * lg_stride_of(capacity, nr) * sizeof(float)) +
+           (size_t)units * g * 2 * sizeof(float);
+}
+
 int decode_max_capacity(int g) {
     (void)g;
     return (kMaxSplit - 1) * kMaxWaveChunk * kWaves;
@@ -921,7 +986,8 @@ int decode_max_capacity(int g) {
 hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
                          int n_packed, int n_res, const CacheView &c,
                          const uint16_t *k_new, const uint16_t *v_new,
-                         void *ws, size_t ws_bytes, hipStream_t stream) {
+                         void *ws, size_t ws_bytes, hipStream_t stream,
+                         const MassOut *mo) {
     DecArgs a;
     a.q = q;
     a.o = o;
@@ -939,8 +1005,20 @@ hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
         return hipErrorInvalidValue;
     a.part_ml = static_cast<float *>(ws);
     a.part_o = a.part_ml + (size_t)units * a.nsplit * g * 2;
-    return c.D == 128 ? launch_decode_d<128>(a, units, g, stream)
-                      : launch_decode_d<64>(a, units, g, stream);
+    a.lg = nullptr;
+    a.lg_stride = 0;
+    float *ml_out = nullptr;
+    if (mo) {
+        if (decode_mass_ws_bytes(units, g, c.D, c.cap, c.nr) > ws_bytes)
+            return hipErrorInvalidValue;
+        char *base = static_cast<char *>(ws) + align256(decode_ws_bytes(units, g, c.D, c.cap));
+        a.lg_stride = lg_stride_of(c.cap, c.nr);
+        a.lg = reinterpret_cast<float *>(base);
+        ml_out = reinterpret_cast<float *>(
+            base + align256((size_t)units * g * a.lg_stride * sizeof(float)));
+    }
+    return c.D == 128 ? launch_decode_d<128>(a, units, g, ml_out, mo, stream)
+                      : launch_decode_d<64>(a, units, g, ml_out, mo, stream);
 }
 
 }  // namespace minikv

@@ -47,13 +47,23 @@ hipError_t launch_append_copy(const uint16_t *k_new, const uint16_t *v_new,
 // Decode attention: q, o [units*g][D].  Caches up to decode_max_capacity(g)
 // packed tokens per unit.
 size_t decode_ws_bytes(int units, int g, int D, int capacity);
+size_t decode_mass_ws_bytes(int units, int g, int D, int capacity, int nr);
 int decode_max_capacity(int g);
+// Persistence audit output: mass[unit * stride + t] += the attention weight
+// of cache token t summed over the unit's g heads.
+struct MassOut {
+    float *mass;
+    int stride;
+};
 // k_new/v_new [units][D] (nullable): a token appended in the same launch; it
-// is residual slot n_res - 1 and is stored there by the kernel.
+// is residual slot n_res - 1 and is stored there by the kernel.  mo
+// (nullable) asks for the mass audit; ws must then hold
+// decode_mass_ws_bytes.
 hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
                          int n_packed, int n_res, const CacheView &c,
                          const uint16_t *k_new, const uint16_t *v_new,
-                         void *ws, size_t ws_bytes, hipStream_t stream);
+                         void *ws, size_t ws_bytes, hipStream_t stream,
+                         const MassOut *mo = nullptr);
 
 // Prefill, both passes.
 hipError_t launch_prefill(const uint16_t *q, const uint16_t *k,

@@ -71,6 +71,7 @@ def lib():
             "minikv_cache_layout": ([D, _i32, _P], _i32),
             "minikv_prefill_ws_bytes": ([D, _i32, _i32, _P], _i32),
             "minikv_decode_ws_bytes": ([D, _i32, _P], _i32),
+            "minikv_decode_mass_ws_bytes": ([D, _i32, _P], _i32),
             "minikv_prefill_attn": ([D, _i32, _P, _P, _P, _P, _P, _P, _P],
                                     _i32),
             "minikv_select": ([D, _i32, _P, _i32, _i32, _P, _P], _i32),
@@ -79,6 +80,8 @@ def lib():
             "minikv_pack": ([D, _i32, _P, _P, _P, _i32, C, _P], _i32),
             "minikv_append": ([D, C, _P, _P, _P], _i32),
             "minikv_decode_attn": ([D, C, _P, _P, _P, _sz, _P], _i32),
+            "minikv_decode_attn_mass": ([D, C, _P, _P, _P, _i32, _P, _sz, _P],
+                                        _i32),
             "minikv_append_decode": ([D, C, _P, _P, _P, _P, _P, _sz, _P],
                                      _i32),
         }
@@ -95,7 +98,8 @@ EXPORTED = ("minikv_version", "minikv_status_str", "minikv_last_error",
             "minikv_cache_layout", "minikv_prefill_ws_bytes",
             "minikv_decode_ws_bytes", "minikv_prefill_attn", "minikv_select",
             "minikv_prefill_select", "minikv_pack", "minikv_append",
-            "minikv_decode_attn", "minikv_append_decode")
+            "minikv_decode_attn", "minikv_append_decode",
+            "minikv_decode_mass_ws_bytes", "minikv_decode_attn_mass")
 
 
 def status_str(s):
@@ -296,6 +300,33 @@ def append(dims, cache, k_new, v_new, stream=None):
     _need(v_new, torch.float16, shape, "v_new")
     _check(lib().minikv_append(ctypes.byref(dims), ctypes.byref(cache.c),
                                _ptr(k_new), _ptr(v_new), _stream(stream)))
+
+
+def decode_mass_ws_bytes(dims, capacity):
+    out = ctypes.c_size_t()
+    _check(lib().minikv_decode_mass_ws_bytes(
+        ctypes.byref(dims), capacity, ctypes.cast(ctypes.pointer(out), _P)))
+    return out.value
+
+
+def decode_attn_mass(dims, cache, q, mass, o=None, ws=None, stream=None):
+    """decode_attn(q), and mass[b, kvh, t] += the attention weight of cache
+    token t summed over the kv head's query heads (persistence audit).
+    mass: fp32 [B][Hkv][stride], stride >= n_packed + n_res."""
+    shape = (dims.batch, dims.n_q_heads, dims.head_dim)
+    _need(q, torch.float16, shape, "q")
+    if (mass.dtype != torch.float32 or mass.dim() != 3 or not mass.is_contiguous()
+            or tuple(mass.shape[:2]) != (dims.batch, dims.n_kv_heads)):
+        raise ValueError("mass: contiguous fp32 [B][Hkv][stride] expected")
+    o = torch.empty_like(q) if o is None else o
+    if ws is None:
+        ws = torch.empty(decode_mass_ws_bytes(dims, cache.capacity),
+                         dtype=torch.uint8, device=q.device)
+    _check(lib().minikv_decode_attn_mass(
+        ctypes.byref(dims), ctypes.byref(cache.c), _ptr(q), _ptr(o),
+        _ptr(mass), mass.shape[2], _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+    return o
 
 
 def decode_attn(dims, cache, q, o=None, ws=None, stream=None):

@@ -179,3 +179,29 @@ def test_decode_workspace_sizes(mk):
     d = mk.make_dims(1, 32, 8, 128)
     ws = mk.decode_ws_bytes(d, 131072)
     assert 0 < ws < 64 * 2 ** 20
+
+
+def test_decode_mass_validation(mk):
+    """minikv_decode_attn_mass rejects a missing mass array, a stride shorter
+    than the cached tokens and a workspace without room for the logits,
+    all before any HIP call."""
+    L = mk.lib()
+    d = mk.make_dims(1, 4, 2, 128, 16, 16, 128)
+    fake = 0x1000
+    by = ctypes.byref
+    P = ctypes.c_void_p
+    c = mk._CacheC(*([fake] * 8), 256, 64, 5)
+    big = mk.decode_mass_ws_bytes(d, 256)
+    assert big > mk.decode_ws_bytes(d, 256)
+    # logits of every (unit, head, token slot) fit: 2 units x 2 heads x 384
+    assert big >= mk.decode_ws_bytes(d, 256) + 2 * 2 * (256 + 128) * 4
+    rc = L.minikv_decode_attn_mass(by(d), by(c), P(fake), P(fake), None, 100,
+                                   P(fake), big, None)
+    assert rc == mk.EINVAL and b"mass" in L.minikv_last_error()
+    rc = L.minikv_decode_attn_mass(by(d), by(c), P(fake), P(fake), P(fake),
+                                   68, P(fake), big, None)
+    assert rc == mk.EINVAL and b"mass_stride" in L.minikv_last_error()
+    rc = L.minikv_decode_attn_mass(by(d), by(c), P(fake), P(fake), P(fake),
+                                   69, P(fake), mk.decode_ws_bytes(d, 256),
+                                   None)
+    assert rc == mk.EINVAL and b"workspace" in L.minikv_last_error()

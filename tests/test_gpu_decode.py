@@ -228,3 +228,57 @@ def test_append_decode_equals_separate_calls(g, D):
             xa, xb = cache_to_numpy(ca), cache_to_numpy(cb)
             for name in xa:
                 assert np.array_equal(xa[name], xb[name]), (s, name)
+
+
+@pytest.mark.parametrize("B,Hkv,g,D,Gk,Gv,n,m", [
+    (1, 2, 1, 128, 16, 16, 900, 500),     # single-batch waves
+    (1, 2, 4, 64, 32, 16, 900, 500),
+    (2, 2, 2, 128, 16, 32, 700, 330),
+    (8, 32, 1, 128, 16, 16, 2200, 2100),  # multi-batch waves
+])
+def test_decode_mass_matches_oracle(B, Hkv, g, D, Gk, Gv, n, m):
+    """Persistence audit: minikv_decode_attn_mass gives decode_attn's o bit
+    for bit, and accumulates every cached token's attention weight (summed
+    over the kv head's query heads) in cache order; over steps that cross a
+    residual flush the accumulated mass matches the oracle's weights summed
+    the same way, within 1e-3 relative + 1e-6 per step, and sums to g per
+    step."""
+    torch, mk = require_gpu()
+    say("decode-mass", dict(B=B, Hkv=Hkv, g=g, D=D, Gk=Gk, Gv=Gv, n=n, m=m))
+    units = [(b, h) for b in range(B) for h in range(Hkv)]
+    if len(units) > 8:
+        rr = np.random.default_rng(m)
+        units = [units[i] for i in sorted(rr.choice(len(units), 8, replace=False))]
+    dims, cache, oc = _build(torch, mk, B, Hkv, g, D, Gk, Gv, n, m,
+                             seed=60 + g + D, check_bits=False, units=units)
+    stride = cache.capacity + dims.residual_cap
+    mass = torch.zeros(B, Hkv, stride, dtype=torch.float32, device="cuda")
+    ref = np.zeros((B, Hkv, stride))
+    steps = 0
+    for s_ in range(132 - cache.n_res):          # the last step flushes
+        q, kn, vn = synth.gen_decode_step(13, 0, s_, B, Hkv * g, Hkv, D)
+        mk.append(dims, cache, dev16(torch, kn), dev16(torch, vn))
+        oc.append(kn, vn)
+        if s_ % 40 and oc.n_res != 0:
+            continue
+        qd = dev16(torch, q)
+        o = mk.decode_attn_mass(dims, cache, qd, mass)
+        o_plain = mk.decode_attn(dims, cache, qd)
+        assert torch.equal(o.view(torch.int16), o_plain.view(torch.int16))
+        steps += 1
+        T = oc.n_packed + oc.n_res
+        with cf.ThreadPoolExecutor(WORKERS) as ex:
+            outs = list(ex.map(lambda u: oc.decode_unit(
+                q[u[0], u[1] * g:(u[1] + 1) * g], u[0], u[1], with_mass=True),
+                units))
+        for (b, h), (ro, rm) in zip(units, outs):
+            assert_close(o.cpu().numpy()[b, h * g:(h + 1) * g], ro,
+                         "decode o[b=%d,kvh=%d]" % (b, h))
+            ref[b, h, :T] += rm
+    got = mass.cpu().numpy().astype(np.float64)
+    for b, h in units:
+        err = np.abs(got[b, h] - ref[b, h])
+        bad = err > 1e-3 * np.abs(ref[b, h]) + 1e-6 * steps
+        assert not bad.any(), ("mass", b, h, int(np.argmax(err)), err.max())
+        assert abs(got[b, h].sum() - g * steps) <= 1e-4 * g * steps
+    say("decode-mass steps", steps)
