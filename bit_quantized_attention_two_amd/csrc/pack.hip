@@ -63,9 +63,13 @@ __device__ __forceinline__ void unpack8(uint4 x, float *f) {
 }
 
 // Keys: one thread per (key group, 8 channels), 16-byte loads of each of the
-// group's Gk source rows, eight rows in flight at a time (read twice:
-// min/max, then codes; the second read hits the cache).  A key word holds 16 channels of one token, so the two
-// threads of a 16-channel block combine their halves of each word.
+// group's Gk source rows.  Rows come sixteen at a time: the sixteen
+// selection indices are requested together, then the sixteen rows, so a
+// 16-token group costs two round trips to memory and its rows stay in
+// registers for both the min/max pass and the code pass (longer groups
+// read each 16-row chunk again for the codes; the second read hits the
+// cache).  A key word holds 16 channels of one token, so the two threads of
+// a 16-channel block combine their halves of each word.
 template <int D>
 __global__ __launch_bounds__(256) void pack_keys_kernel(
     PackSrc src, int n_groups, int dst_group_off, CacheView c) {
@@ -81,19 +85,19 @@ __global__ __launch_bounds__(256) void pack_keys_kernel(
                                  : nullptr;
     const int p0 = gi * Gk;
 
-    // rows are loaded RB at a time, so that their latencies overlap
-    constexpr int RB = 8;                        // Gk is a multiple of 16
-    auto load_rows = [&](int t0, uint4 (&r)[RB]) {
+    constexpr int RB = 16;                       // Gk is a multiple of 16
+    uint4 rr[RB];
+    auto load_rows = [&](int t0) {
+        int row[RB];
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            const int row = sel ? sel[p0 + t0 + i] : p0 + t0 + i;
-            r[i] = *reinterpret_cast<const uint4 *>(base + (size_t)row * D);
-        }
+        for (int i = 0; i < RB; ++i) row[i] = sel ? sel[p0 + t0 + i] : p0 + t0 + i;
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+            rr[i] = *reinterpret_cast<const uint4 *>(base + (size_t)row[i] * D);
     };
     float mn[8], mx[8];
     for (int t0 = 0; t0 < Gk; t0 += RB) {
-        uint4 rr[RB];
-        load_rows(t0, rr);
+        load_rows(t0);
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
             float x[8];
@@ -119,8 +123,7 @@ __global__ __launch_bounds__(256) void pack_keys_kernel(
                   (size_t)g_out * Gk * (D / 16) + oct / 2;
     const int sh = 16 * (oct & 1);               // this thread's half-word
     for (int t0 = 0; t0 < Gk; t0 += RB) {
-        uint4 rr[RB];
-        load_rows(t0, rr);
+        if (Gk > RB) load_rows(t0);              // a 16-token group kept its rows
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
             float x[8];
@@ -148,13 +151,34 @@ __global__ __launch_bounds__(256) void pack_keys_kernel(
 // 16 lanes of a DPP row take 16 consecutive tokens of the same channel group
 // and OR their codes together, lane e keeping the words of channels
 // 16 j + e of the group.  Token counts are multiples of 16.
+//
+// The threads after the packed tokens' ones copy the next n_tail source
+// rows of K and V, unchanged, into residual slots 0..n_tail-1 (the ragged
+// tail of the selection stays fp16), 16 bytes each.  The boundary falls on
+// a multiple of 16 threads, so no DPP row mixes the two kinds.
 template <int D>
 __global__ __launch_bounds__(256) void pack_values_kernel(
-    PackSrc src, int n_tok, int dst_off, CacheView c) {
+    PackSrc src, int n_tok, int n_tail, int dst_off, CacheView c) {
     const int unit = blockIdx.y;
     const int Gv = c.Gv;
     const int gpt = D / Gv;                      // groups per token
     const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n_tok * gpt) {
+        constexpr int PER_ROW = D / 8;           // uint4 per row
+        const int tidx = idx - n_tok * gpt;
+        const int slot = tidx / PER_ROW;
+        const int part = tidx % PER_ROW;
+        if (slot >= n_tail) return;
+        const int p = n_tok + slot;
+        const int row = src.sel ? src.sel[(size_t)unit * src.sel_unit + p] : p;
+        const size_t s_off = (size_t)unit * src.src_unit + (size_t)row * D;
+        const size_t d_off = (size_t)unit * c.res_unit() + (size_t)slot * D;
+        reinterpret_cast<uint4 *>(c.kres + d_off)[part] =
+            reinterpret_cast<const uint4 *>(src.k + s_off)[part];
+        reinterpret_cast<uint4 *>(c.vres + d_off)[part] =
+            reinterpret_cast<const uint4 *>(src.v + s_off)[part];
+        return;
+    }
     const int e = idx & 15;                      // token within its block
     const int bg = idx >> 4;
     const int blk = bg / gpt;                    // 16-token block
@@ -202,25 +226,6 @@ __global__ __launch_bounds__(256) void pack_values_kernel(
     c.vz[mo] = qp.zh;
 }
 
-// Copy n_tail source rows (after the packed ones) into residual slots.
-__global__ __launch_bounds__(256) void copy_tail_kernel(
-    PackSrc src, int p_first, int n_tail, CacheView c) {
-    const int unit = blockIdx.y;
-    const int per_row = c.D / 8;                 // uint4 per row
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    const int slot = idx / per_row;
-    const int part = idx % per_row;
-    if (slot >= n_tail) return;
-    const int p = p_first + slot;
-    const int row = src.sel ? src.sel[(size_t)unit * src.sel_unit + p] : p;
-    const size_t s_off = (size_t)unit * src.src_unit + (size_t)row * c.D;
-    const size_t d_off = (size_t)unit * c.res_unit() + (size_t)slot * c.D;
-    reinterpret_cast<uint4 *>(c.kres + d_off)[part] =
-        reinterpret_cast<const uint4 *>(src.k + s_off)[part];
-    reinterpret_cast<uint4 *>(c.vres + d_off)[part] =
-        reinterpret_cast<const uint4 *>(src.v + s_off)[part];
-}
-
 __global__ __launch_bounds__(256) void append_copy_kernel(
     const uint16_t *k_new, const uint16_t *v_new, int units, int slot,
     CacheView c) {
@@ -244,24 +249,19 @@ hipError_t launch_pack(const PackSrc &src, int units, int n_tok, int n_tail,
         const int n_groups = n_tok / c.Gk;
         const int gpb = 256 / (c.D / 8);
         dim3 gk((n_groups + gpb - 1) / gpb, units);
-        const int vthreads = n_tok * (c.D / c.Gv);   // n_tok % 16 == 0
-        dim3 gv((vthreads + 255) / 256, units);
-        if (c.D == 128) {
-            pack_keys_kernel<128><<<gk, 256, 0, stream>>>(
-                src, n_groups, dst_off / c.Gk, c);
-            pack_values_kernel<128><<<gv, 256, 0, stream>>>(src, n_tok,
-                                                            dst_off, c);
-        } else {
-            pack_keys_kernel<64><<<gk, 256, 0, stream>>>(
-                src, n_groups, dst_off / c.Gk, c);
-            pack_values_kernel<64><<<gv, 256, 0, stream>>>(src, n_tok,
-                                                           dst_off, c);
-        }
+        if (c.D == 128)
+            pack_keys_kernel<128><<<gk, 256, 0, stream>>>(src, n_groups, dst_off / c.Gk, c);
+        else
+            pack_keys_kernel<64><<<gk, 256, 0, stream>>>(src, n_groups, dst_off / c.Gk, c);
     }
-    if (n_tail > 0) {
-        const int threads = n_tail * (c.D / 8);
-        dim3 gt((threads + 255) / 256, units);
-        copy_tail_kernel<<<gt, 256, 0, stream>>>(src, n_tok, n_tail, c);
+    if (n_tok + n_tail > 0) {
+        // packed tokens' value threads (n_tok % 16 == 0), then the tail copy
+        const int vthreads = n_tok * (c.D / c.Gv) + n_tail * (c.D / 8);
+        dim3 gv((vthreads + 255) / 256, units);
+        if (c.D == 128)
+            pack_values_kernel<128><<<gv, 256, 0, stream>>>(src, n_tok, n_tail, dst_off, c);
+        else
+            pack_values_kernel<64><<<gv, 256, 0, stream>>>(src, n_tok, n_tail, dst_off, c);
     }
     return hipGetLastError();
 }
