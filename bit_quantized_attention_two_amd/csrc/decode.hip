@@ -35,6 +35,9 @@
 // its softmax statistics, then P.V (phase V); the block merges its waves in
 // LDS and writes one partial (max, sum, unnormalised o) to the workspace.
 // A second kernel merges the partials of each (unit, head) and writes o.
+// Small calls (64 tokens per wave) use a form that requests all of a
+// wave's loads at once (ONE below); the persistence audit adds a third
+// kernel that turns stored logits into per-token attention mass.
 //
 // Fused append: when the caller passes a new token, the residual block reads
 // it from the call's input, uses it as residual slot `new_slot`, and stores
