@@ -53,6 +53,10 @@ def parse():
     p.add_argument("--eager", action="store_true",
                    help="launch every call from Python instead of replaying "
                         "the captured HIP graphs of a step")
+    p.add_argument("--decode-probe", type=int, default=0, metavar="N",
+                   help="run only the decode-call timing at layer 0 of "
+                        "workload N (two alternating caches) and print it; "
+                        "the workload for the decode kernels' counters")
     p.add_argument("--no-large-decode", action="store_true",
                    help="skip the decode-call timing at the 13B-shaped "
                         "batched layer (16 x 40 kv heads, 4096 packed tokens)")
@@ -134,22 +138,25 @@ def traffic_probe():
                       "algorithmic_bytes_per_call": alg / L}), flush=True)
 
 
-def large_decode_roofline(stream):
-    """Decode-attention call at the Llama2-13B-shaped batched layer (batch
-    16, 40 heads, D 128, Gk = Gv = 16): 4096 selected tokens packed plus 64
-    residual tokens per kv head, the state halfway through its decode steps.
-    One call moves ~360 MB, so this is the call in its bandwidth regime; the
-    bench workload's 4096-token layer (~9 MB per call) is latency-bound.
-    Two such caches alternate (720 MB, more than the 256 MB last-level
-    cache, so no call finds the previous call's data there), timed as a
-    graph of back-to-back calls between HIP events on `stream`; the median
-    of 5 replays is reported."""
+def layer_decode_roofline(stream, config_id=3):
+    """Decode-attention call at one layer of a workload, in its bandwidth
+    regime: layer 0's selection (its heavy-hitter budget plus the recent
+    window) packed, then enough decode-step tokens appended to hold 64 in
+    the fp16 residual.  At the Llama2-13B-shaped batched layer (batch 16, 40
+    kv heads, D 128) that is 4096 packed + 64 residual tokens per kv head,
+    ~360 MB per call; the bench workload's 4096-token layer (~9 MB per call)
+    is latency-bound instead.  Two such caches alternate (more than the
+    256 MB last-level cache at the 13B shape, so no call finds the previous
+    call's data there), timed as a graph of back-to-back calls between HIP
+    events on `stream`; the median of 5 replays is reported."""
     import torch
     from bit_quantized_attention_two_amd import configs, minikv
-    c = configs.get(3)
-    B, Hq, Hkv, D, n = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"]
+    c = configs.get(config_id)
+    B, Hq, Hkv, D, n, L = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"], c["L"]
     dims = minikv.make_dims(B, Hq, Hkv, D, c["Gk"], c["Gv"], c["residual_cap"])
-    m, res = 4096, 64
+    ks, r = minikv.pyramid_budgets(n, L, c["hh"], c["rw"], c["depth"],
+                                   c["pyramid"])
+    m, res = ks[0] + r, 64
     g = torch.Generator(device="cuda").manual_seed(3)
     k = torch.randn(B, Hkv, n, D, device="cuda", generator=g).half()
     v = torch.randn(B, Hkv, n, D, device="cuda", generator=g).half()
@@ -157,14 +164,15 @@ def large_decode_roofline(stream):
            ).int().repeat(B, Hkv, 1).contiguous()
     caches = []
     for i in range(2):
-        cache = minikv.LayerCache(dims, m + 256)
+        cache = minikv.LayerCache(dims, (m // c["Gk"]) * c["Gk"] + 256)
         minikv.pack(dims, k, v, (sel + i) % n, cache)
-        for t in range(res):                     # 64 decode-step tokens
+        for t in range(res - cache.n_res):       # decode-step tokens
             minikv.append(dims, cache, k[:, :, t].contiguous(),
                           v[:, :, t].contiguous())
-        assert cache.n_packed == m and cache.n_res == res
+        assert cache.n_res == res
         caches.append(cache)
     del k, v
+    n_packed = caches[0].n_packed
     q = torch.randn(B, Hq, D, device="cuda", generator=g).half()
     o = torch.empty_like(q)
     ws = torch.zeros(minikv.decode_ws_bytes(dims, caches[0].capacity),
@@ -188,12 +196,13 @@ def large_decode_roofline(stream):
         b.record(stream)
     torch.cuda.synchronize()
     us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 / R
-    alg = decode_bytes(c, m, res)
+    alg = decode_bytes(c, n_packed, res)
     achieved = alg / (us * 1e-6) / 1e9
     return {"kernel": "minikv_decode_attn (split-KV decode + combine "
                       "kernels)",
-            "workload": "llama2-13b-8k batched decode layer: batch 16, 40 "
-                        "kv heads, D 128, 4096 packed + 64 residual tokens",
+            "workload": "%s layer 0: batch %d, %d kv heads, g %d, D %d, %d "
+                        "packed + %d residual tokens per kv head" % (
+                            c["name"], B, Hkv, Hq // Hkv, D, n_packed, res),
             "bound": "hbm", "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -221,6 +230,11 @@ def main():
     args = parse()
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.decode_probe:
+        import torch
+        print(json.dumps(layer_decode_roofline(torch.cuda.current_stream(),
+                                               args.decode_probe)), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -467,7 +481,7 @@ def main():
     if not args.no_large_decode:
         del qkv, outs, cols, graphs, g_kern, g_mass
         torch.cuda.empty_cache()
-        result["roofline_decode_large"] = large_decode_roofline(stream)
+        result["roofline_decode_large"] = layer_decode_roofline(stream, 3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, c, ks, r, args.cpu_seconds)
     print(json.dumps(result), flush=True)
