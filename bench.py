@@ -57,6 +57,10 @@ def parse():
                    help="run only the decode-call timing at layer 0 of "
                         "workload N (two alternating caches) and print it; "
                         "the workload for the decode kernels' counters")
+    p.add_argument("--no-persistence", action="store_true",
+                   help="skip the persistence audit (re-selection every 32 "
+                        "decode steps, overlap with the prefill heavy "
+                        "hitters)")
     p.add_argument("--no-large-decode", action="store_true",
                    help="skip the decode-call timing at the 13B-shaped "
                         "batched layer (16 x 40 kv heads, 4096 packed tokens)")
@@ -208,6 +212,56 @@ def layer_decode_roofline(stream, config_id=3):
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(us, 3),
             "algorithmic_bytes_per_launch": int(alg), "launches": R}
+
+
+def persistence_audit(config_id, layer=0, every=32):
+    """The persistence test the MiniKV verdict record's falsifier asks for,
+    on this workload's synthetic inputs: would the heavy hitters chosen at
+    the end of prefill still be chosen later in decoding?  H2O's cumulative
+    score at decode step s is the column sum of causal attention over the
+    prompt plus the first s generated tokens (their q, k, v are the decode
+    steps' inputs), so the selection that step s would make is the library's
+    own prefill+select over that extended sequence, with the candidates kept
+    to the prompt's [0, n - r) (recent window r + s).  Reported: the mean
+    and minimum over kv heads of |HH_s ∩ HH_0| / k every `every` steps, and
+    the time of one re-selection at the last step."""
+    import torch
+    from bit_quantized_attention_two_amd import configs, minikv, synth
+    c = configs.get(config_id)
+    B, Hq, Hkv, D, n, L = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"], c["L"]
+    S = c["decode_steps"]
+    ks, r = minikv.pyramid_budgets(n, L, c["hh"], c["rw"], c["depth"],
+                                   c["pyramid"])
+    n_hh = int(ks[layer])
+    dims = minikv.make_dims(B, Hq, Hkv, D, c["Gk"], c["Gv"], c["residual_cap"])
+    q, k, v = synth.gen_prefill(config_id, layer)
+    steps = [synth.gen_decode_step(config_id, layer, t, B, Hq, Hkv, D)
+             for t in range(S)]
+    ext = [np.concatenate([x, np.stack([st[i] for st in steps], axis=2)],
+                          axis=2) for i, x in enumerate((q, k, v))]
+    Q, K, V = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in ext)
+    points = list(range(0, S + 1, every))
+    if points[-1] != S:
+        points.append(S)
+    hh0, rows, ms = None, [], 0.0
+    for t in points:
+        sub = [x[:, :, :n + t].contiguous() for x in (Q, K, V)]
+        a, b = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        a.record()
+        _, _, sel = minikv.prefill_select(dims, *sub, n_hh, r + t)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        hh = sel[..., :n_hh].cpu().numpy().reshape(B * Hkv, n_hh)
+        if hh0 is None:
+            hh0 = hh
+        ov = np.array([np.intersect1d(x, y).size for x, y in zip(hh, hh0)]) / n_hh
+        rows.append((t, float(ov.mean()), float(ov.min())))
+    return {"layer": layer, "heavy_hitters": n_hh, "recent": r,
+            "steps": [x[0] for x in rows],
+            "overlap_mean": [round(x[1], 4) for x in rows],
+            "overlap_min": [round(x[2], 4) for x in rows],
+            "reselect_ms_at_last_step": round(ms, 3)}
 
 
 def decode_bytes(c, n_packed, n_res):
@@ -478,6 +532,8 @@ def main():
         },
         "input_generation_s": round(gen_s, 1),
     }
+    if not args.no_persistence:
+        result["persistence_audit"] = persistence_audit(args.config)
     if not args.no_large_decode:
         del qkv, outs, cols, graphs, g_kern, g_mass
         torch.cuda.empty_cache()

@@ -111,3 +111,49 @@ def test_pipeline(cfg_id, layer):
                 assert_close(od[b, h * g:(h + 1) * g],
                              ref[b, h * g:(h + 1) * g], "decode step %d" % s)
     assert cache.n_packed == oc.n_packed and cache.n_res == oc.n_res
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2])
+def test_persistence_reselection(cfg_id):
+    """Persistence audit: the selection decode step s would make (prefill +
+    select over the prompt plus the first s generated tokens, candidates
+    kept to the prompt's [0, n - r)) matches the oracle's on the same
+    extended sequence, under the selection protocol above, at s = 0, the
+    middle and the last decode step; the overlap with the prefill-time heavy
+    hitters is then the same for both."""
+    torch, mk = require_gpu()
+    c = configs.get(cfg_id)
+    B, Hq, Hkv, D, n, g = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"], c["g"]
+    ks, r = oracle.budgets(n, c["L"], c["depth"], c["pyramid"])
+    n_hh = int(ks[0])
+    S = c["decode_steps"]
+    q, k, v = synth.gen_prefill(cfg_id, 0)
+    st = [synth.gen_decode_step(cfg_id, 0, t, B, Hq, Hkv, D) for t in range(S)]
+    ext = [np.ascontiguousarray(np.concatenate(
+        [x, np.stack([s_[i] for s_ in st], axis=2)], axis=2))
+        for i, x in enumerate((q, k, v))]
+    dims = mk.make_dims(B, Hq, Hkv, D, c["Gk"], c["Gv"], c["residual_cap"])
+    units = [(b, h) for b in range(B) for h in range(Hkv)]
+    if len(units) > 4:                     # the oracle's prefill is O(n^2 D)
+        units = units[:2] + units[-2:]
+    hh0_g, hh0_o = {}, {}
+    for t in (0, S // 2, S):
+        say("persistence", dict(cfg=cfg_id, step=t))
+        sub = [np.ascontiguousarray(x[:, :, :n + t]) for x in ext]
+        _, col, sel = mk.prefill_select(dims, *[dev16(torch, x) for x in sub],
+                                        n_hh, r + t)
+        col, sel = col.cpu().numpy(), sel.cpu().numpy()
+        with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+            refs = list(ex.map(lambda u: oracle.prefill_unit(
+                sub[0][u[0], u[1] * g:(u[1] + 1) * g], sub[1][u[0], u[1]],
+                sub[2][u[0], u[1]]), units))
+        for (b, h), (_, _, rc) in zip(units, refs):
+            osel = oracle.select(rc, n_hh, r + t)
+            swaps = _check_selection(sel[b, h], col[b, h], osel, rc, n_hh, r + t)
+            if t == 0:
+                if swaps == 0:
+                    hh0_g[b, h], hh0_o[b, h] = sel[b, h, :n_hh], osel[:n_hh]
+            elif swaps == 0 and (b, h) in hh0_g:
+                og = np.intersect1d(sel[b, h, :n_hh], hh0_g[b, h]).size
+                oo = np.intersect1d(osel[:n_hh], hh0_o[b, h]).size
+                assert og == oo
