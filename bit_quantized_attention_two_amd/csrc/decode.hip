@@ -55,12 +55,18 @@ constexpr int kWaves = 4;
 constexpr int kMinWaveChunk = 64;
 constexpr int kMaxWaveChunk = 256;
 constexpr int kMaxSplit = 512;
+// GQA calls whose grid fills the chip in one round use one 12-wave block
+// per CU (launch_decode explains why); its splits are 12 * 256 tokens.
+constexpr int kBigWaves = 12;
+constexpr int kBigChunk = kBigWaves * kMaxWaveChunk;
 
 struct DecArgs {
     const uint16_t *q;
     uint16_t *o;
     CacheView c;
     int n_packed, n_res, chunk, n_chunks, nsplit;
+    int res_split, res_wave0;        // the residual's waves: split res_split,
+                                     // waves res_wave0.. (-1: no residual)
     float qscale;
     const uint16_t *k_new, *v_new;   // nullable: fused append of one token
     int new_slot;                    // residual slot of the new token
@@ -721,8 +727,9 @@ __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0
 
 // FULLV: value channel groups of 16 (D/16 scales per token).
 // MASS: also store every token's logit for the persistence audit.
-template <int D, int G, bool FULLV, bool ONE, bool MASS>
-__global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_kernel(DecArgs a) {
+// W: waves per block, each with a chunk / W share of the split's tokens.
+template <int D, int G, bool FULLV, bool ONE, bool MASS, int W = kWaves>
+__global__ __launch_bounds__(W * 64, (G == 2 || G == 8) ? 2 : 3) void decode_kernel(DecArgs a) {
     // x = unit, y = split: with the round-robin dispatch of workgroups over
     // the 8 XCDs, every split of a unit (and its merge below) runs on the
     // XCD unit mod 8 when the unit count is a multiple of 8.
@@ -733,8 +740,8 @@ __global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_k
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const CacheView &c = a.c;
 
-    __shared__ WaveLds<D, G> lds[kWaves];
-    __shared__ float red_ml[kWaves][G][2];
+    __shared__ WaveLds<D, G> lds[W];
+    __shared__ float red_ml[W][G][2];
     __shared__ float mrg[G][2];
 
     float m_w[G], l_w[G];
@@ -743,18 +750,23 @@ __global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_k
         m_w[h] = -INFINITY;
         l_w[h] = 0.f;
     }
-    if (split < a.n_chunks) {
-        const int wchunk = a.chunk / kWaves;
+    // The fp16 residual runs on waves res_wave0.. of split res_split: the
+    // idle waves of the last packed split when they have room, else a split
+    // of its own.
+    const bool res_role = split == a.res_split && wave >= a.res_wave0;
+    if (!res_role && split < a.n_chunks) {
+        const int wchunk = a.chunk / W;
         const int t0 = split * a.chunk + wave * wchunk;
         const int nt = max(0, min(wchunk, a.n_packed - t0));
         if (nt > 0) packed_wave<D, G, FULLV, ONE, MASS>(a, unit, t0, nt, lds[wave], m_w, l_w);
-    } else {
-        const int per = (a.n_res + kWaves - 1) / kWaves;
-        const int t0 = wave * per;
+    } else if (res_role) {
+        const int nrw = W - a.res_wave0, rw = wave - a.res_wave0;
+        const int per = (a.n_res + nrw - 1) / nrw;
+        const int t0 = rw * per;
         const int nt = max(0, min(per, a.n_res - t0));
         if (nt > 0) residual_wave<D, G, MASS>(a, unit, t0, nt, lds[wave], m_w, l_w);
         // store the new token into its residual slot for later calls
-        if (a.k_new && wave == 0 && lane < 2 * (D / 8)) {
+        if (a.k_new && rw == 0 && lane < 2 * (D / 8)) {
             const int part = lane % (D / 8);
             const bool isv = lane >= D / 8;
             const uint16_t *src = (isv ? a.v_new : a.k_new) + (size_t)unit * D;
@@ -774,10 +786,10 @@ __global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_k
     // ----------------------------------------- merge the 4 waves, store
     if (tid < G) {
         float M = -INFINITY;
-        for (int w = 0; w < kWaves; ++w)
+        for (int w = 0; w < W; ++w)
             if (red_ml[w][tid][1] > 0.f) M = fmaxf(M, red_ml[w][tid][0]);
         float L = 0.f;
-        for (int w = 0; w < kWaves; ++w)
+        for (int w = 0; w < W; ++w)
             if (red_ml[w][tid][1] > 0.f)
                 L += red_ml[w][tid][1] * __builtin_amdgcn_exp2f(red_ml[w][tid][0] - M);
         mrg[tid][0] = M;
@@ -785,11 +797,11 @@ __global__ __launch_bounds__(kThreads, (G == 2 || G == 8) ? 2 : 3) void decode_k
     }
     __syncthreads();
     const size_t sbase = (size_t)unit * a.nsplit + split;
-    for (int i = tid; i < G * D; i += kThreads) {
+    for (int i = tid; i < G * D; i += (W * 64)) {
         const int h = i / D;
         const float M = mrg[h][0];
         float v = 0.f;
-        for (int w = 0; w < kWaves; ++w)
+        for (int w = 0; w < W; ++w)
             if (red_ml[w][h][1] > 0.f)
                 v += lds[w].ls[i] * __builtin_amdgcn_exp2f(red_ml[w][h][0] - M);
         a.part_o[sbase * G * D + i] = v;
@@ -899,7 +911,15 @@ __global__ __launch_bounds__(kThreads) void decode_mass_kernel(
 // splits per unit.  A wave's share is a power of two between
 // max(kMinWaveChunk, Gk) and kMaxWaveChunk tokens, so it holds whole key
 // groups and whole 32-token value steps.
-int pick_chunk(int units, int n_packed, int Gk, int g) {
+int pick_chunk(int units, int n_packed, int Gk, int g, bool mass) {
+    // g = 4 with a grid of 12-wave blocks that fills 3/4 to all of the CUs
+    // in one round.  Three 4-wave blocks per CU would all start together,
+    // and the instruction arbiter's preference for older waves then makes
+    // the third block of each CU finish ~35% after the first, so the call
+    // ends with the CUs a third occupied; the waves of one block share one
+    // age and finish together.
+    const long big = (long)units * ((n_packed + kBigChunk - 1) / kBigChunk);
+    if (g == 4 && !mass && Gk <= kMaxWaveChunk && big >= 192 && big <= 256) return kBigChunk;
     const int per_cu = g == 1 ? 4 : g == 4 ? 3 : 2;
     const long want = 256L * per_cu / 2;
     const int minw = std::max(kMinWaveChunk, Gk);
@@ -919,7 +939,18 @@ hipError_t launch_decode_dg(const DecArgs &a, int units, float *ml_out,
     // for g <= 2 (at g = 4 its registers would spill)
     const bool one = G <= 2 && a.chunk == kMinWaveChunk * kWaves;
     const dim3 grid(units, a.nsplit);
-    if (mo) {
+    bool big = false;
+    if constexpr (G == 4) {
+        if (a.chunk == kBigChunk) {
+            big = true;
+            if (a.c.Gv == 16)
+                decode_kernel<D, G, true, false, false, kBigWaves><<<grid, kBigWaves * 64, 0, stream>>>(a);
+            else
+                decode_kernel<D, G, false, false, false, kBigWaves><<<grid, kBigWaves * 64, 0, stream>>>(a);
+        }
+    }
+    if (big) {
+    } else if (mo) {
         if (a.c.Gv == 16) {
             if (one) decode_kernel<D, G, true, G <= 2, true><<<grid, kThreads, 0, stream>>>(a);
             else decode_kernel<D, G, true, false, true><<<grid, kThreads, 0, stream>>>(a);
@@ -997,9 +1028,27 @@ hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
     a.c = c;
     a.n_packed = n_packed;
     a.n_res = n_res;
-    a.chunk = pick_chunk(units, n_packed, c.Gk, g);
+    a.chunk = pick_chunk(units, n_packed, c.Gk, g, mo != nullptr);
     a.n_chunks = (n_packed + a.chunk - 1) / a.chunk;
-    a.nsplit = a.n_chunks + (n_res > 0 ? 1 : 0);
+    a.nsplit = a.n_chunks;
+    a.res_split = -1;
+    a.res_wave0 = 0;
+    if (n_res > 0) {
+        // waves of 64 residual tokens at most; in the last packed split's
+        // idle waves when there are enough of them
+        const int W = a.chunk == kBigChunk ? kBigWaves : kWaves;
+        const int wchunk = a.chunk / W;
+        const int need = (n_res + 63) / 64;
+        const int used = a.n_chunks > 0
+            ? (n_packed - (a.n_chunks - 1) * a.chunk + wchunk - 1) / wchunk : W;
+        if (W - used >= need) {
+            a.res_split = a.n_chunks - 1;
+            a.res_wave0 = W - need;
+        } else {
+            a.res_split = a.n_chunks;
+            a.nsplit = a.n_chunks + 1;
+        }
+    }
     a.qscale = kLog2e / sqrtf((float)c.D);
     a.k_new = k_new;
     a.v_new = v_new;
