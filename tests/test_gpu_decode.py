@@ -203,18 +203,21 @@ def test_decode_multi_batch_waves(D, g, Gv):
     _decode_and_compare(torch, mk, dims, cache, oc, q, units)
 
 
-@pytest.mark.parametrize("g,D", [(1, 128), (4, 128), (2, 64)])
-def test_append_decode_equals_separate_calls(g, D):
+@pytest.mark.parametrize("g,D,B,Hkv,n,m", [
+    (1, 128, 2, 2, 700, 333), (4, 128, 2, 2, 700, 333), (2, 64, 2, 2, 700, 333),
+    # 32 kv heads x 8 splits of 3072 tokens: the one-round 12-wave GQA form,
+    # with the residual on the last split's idle waves
+    (4, 128, 4, 8, 24000, 23400)])
+def test_append_decode_equals_separate_calls(g, D, B, Hkv, n, m):
     """The fused entry point gives the same bits as minikv_append followed by
     minikv_decode_attn, across a residual flush, and leaves the same cache."""
     torch, mk = require_gpu()
     from gpu_util import cache_to_numpy
-    B, Hkv, n, m = 2, 2, 700, 333
     dims, ca, _ = _build(torch, mk, B, Hkv, g, D, 16, 16, n, m, seed=21,
-                         check_bits=False)
+                         check_bits=False, units=[(0, 0)])
     _, cb, _ = _build(torch, mk, B, Hkv, g, D, 16, 16, n, m, seed=21,
-                      check_bits=False)
-    say("append_decode", dict(g=g, D=D))
+                      check_bits=False, units=[(0, 0)])
+    say("append_decode", dict(g=g, D=D, B=B, Hkv=Hkv, m=m))
     for s in range(140):
         q, kn, vn = synth.gen_decode_step(21, 0, s, B, Hkv * g, Hkv, D)
         q, kn, vn = dev16(torch, q), dev16(torch, kn), dev16(torch, vn)
