@@ -56,9 +56,8 @@ constexpr int kMinWaveChunk = 64;
 constexpr int kMaxWaveChunk = 256;
 constexpr int kMaxSplit = 512;
 // GQA calls whose grid fills the chip in one round use one 12-wave block
-// per CU (launch_decode explains why); its splits are 12 * 256 tokens.
+// per CU (pick_chunk explains why); its splits are 12 wave shares.
 constexpr int kBigWaves = 12;
-constexpr int kBigChunk = kBigWaves * kMaxWaveChunk;
 
 struct DecArgs {
     const uint16_t *q;
@@ -67,6 +66,7 @@ struct DecArgs {
     int n_packed, n_res, chunk, n_chunks, nsplit;
     int res_split, res_wave0;        // the residual's waves: split res_split,
                                      // waves res_wave0.. (-1: no residual)
+    int waves;                       // waves per block: kWaves or kBigWaves
     float qscale;
     const uint16_t *k_new, *v_new;   // nullable: fused append of one token
     int new_slot;                    // residual slot of the new token
@@ -912,24 +912,34 @@ __global__ __launch_bounds__(kThreads) void decode_mass_kernel(
 // max(kMinWaveChunk, Gk) and kMaxWaveChunk tokens, so it holds whole key
 // groups and whole 32-token value steps.
 int pick_chunk(int units, int n_packed, int Gk, int g, bool mass) {
-    // g = 4 with a grid of 12-wave blocks that fills 3/4 to all of the CUs
-    // in one round.  Three 4-wave blocks per CU would all start together,
-    // and the instruction arbiter's preference for older waves then makes
-    // the third block of each CU finish ~35% after the first, so the call
-    // ends with the CUs a third occupied; the waves of one block share one
-    // age and finish together.
-    const long big = (long)units * ((n_packed + kBigChunk - 1) / kBigChunk);
-    if (g == 4 && !mass && Gk <= kMaxWaveChunk && big >= 192 && big <= 256) return kBigChunk;
     const int per_cu = g == 1 ? 4 : g == 4 ? 3 : 2;
     const long want = 256L * per_cu / 2;
     const int minw = std::max(kMinWaveChunk, Gk);
+    int ch4 = minw * kWaves;
     for (int w = kMaxWaveChunk; w > minw; w >>= 1) {
         const int ch = w * kWaves;
         const int next = ch / 2;
-        if ((long)units * ((n_packed + ch - 1) / ch) >= want) return ch;
-        if ((n_packed + next - 1) / next > kMaxSplit - 1) return ch;
+        if ((long)units * ((n_packed + ch - 1) / ch) >= want ||
+            (n_packed + next - 1) / next > kMaxSplit - 1) {
+            ch4 = ch;
+            break;
+        }
     }
-    return minw * kWaves;
+    // g = 4: one 12-wave block per CU when such a grid fills the chip in one
+    // round (240-256 blocks), or fills at least 3/4 of it while the 4-wave
+    // form would need splits of 512 tokens or fewer.  Three 4-wave blocks per
+    // CU all start together, and the instruction arbiter's preference for
+    // older waves then makes the third block of each CU finish ~35% after
+    // the first, so the call ends with the CUs a third occupied; the waves of
+    // one block share one age and finish together.
+    if (g == 4 && !mass) {
+        for (int w = kMaxWaveChunk; w >= minw; w >>= 1) {
+            const long big = (long)units * ((n_packed + kBigWaves * w - 1) / (kBigWaves * w));
+            if (big <= 256 && (big >= 240 || (big >= 192 && ch4 <= 512)))
+                return kBigWaves * w;
+        }
+    }
+    return ch4;
 }
 
 template <int D, int G>
@@ -941,7 +951,7 @@ hipError_t launch_decode_dg(const DecArgs &a, int units, float *ml_out,
     const dim3 grid(units, a.nsplit);
     bool big = false;
     if constexpr (G == 4) {
-        if (a.chunk == kBigChunk) {
+        if (a.waves == kBigWaves) {
             big = true;
             if (a.c.Gv == 16)
                 decode_kernel<D, G, true, false, false, kBigWaves><<<grid, kBigWaves * 64, 0, stream>>>(a);
@@ -1029,6 +1039,7 @@ hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
     a.n_packed = n_packed;
     a.n_res = n_res;
     a.chunk = pick_chunk(units, n_packed, c.Gk, g, mo != nullptr);
+    a.waves = a.chunk % kBigWaves == 0 ? kBigWaves : kWaves;   // W = 4 chunks are 2^k
     a.n_chunks = (n_packed + a.chunk - 1) / a.chunk;
     a.nsplit = a.n_chunks;
     a.res_split = -1;
@@ -1036,7 +1047,7 @@ hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
     if (n_res > 0) {
         // waves of 64 residual tokens at most; in the last packed split's
         // idle waves when there are enough of them
-        const int W = a.chunk == kBigChunk ? kBigWaves : kWaves;
+        const int W = a.waves;
         const int wchunk = a.chunk / W;
         const int need = (n_res + 63) / 64;
         const int used = a.n_chunks > 0

@@ -203,6 +203,23 @@ def test_decode_multi_batch_waves(D, g, Gv):
     _decode_and_compare(torch, mk, dims, cache, oc, q, units)
 
 
+@pytest.mark.parametrize("n,m", [(41000, 40000), (24000, 23400)])
+def test_decode_one_round_gqa(n, m):
+    """g = 4 calls in the one-round 12-wave form: 8 kv heads x 27 splits of
+    1536 tokens (128 per wave; the 4-wave form would need 512-token splits)
+    and 8 kv heads x 31 splits of 768 tokens (64 per wave); every unit
+    against the oracle."""
+    torch, mk = require_gpu()
+    B, Hkv, g, D = 1, 8, 4, 128
+    say("decode-one-round-gqa", dict(n=n, m=m))
+    dims, cache, oc = _build(torch, mk, B, Hkv, g, D, 16, 16, n, m,
+                             seed=90 + m % 7, check_bits=False)
+    q, kn, vn = synth.gen_decode_step(9, 0, 0, B, Hkv * g, Hkv, D)
+    mk.append(dims, cache, dev16(torch, kn), dev16(torch, vn))
+    oc.append(kn, vn)
+    _decode_and_compare(torch, mk, dims, cache, oc, q)
+
+
 @pytest.mark.parametrize("g,D,B,Hkv,n,m", [
     (1, 128, 2, 2, 700, 333), (4, 128, 2, 2, 700, 333), (2, 64, 2, 2, 700, 333),
     # 32 kv heads x 8 splits of 3072 tokens: the one-round 12-wave GQA form,
