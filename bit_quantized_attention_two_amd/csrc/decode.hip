@@ -30,16 +30,18 @@
 // group an MFMA of the zero-points with q, and per token a VALU sum.
 //
 // Work split: block (unit, split) covers `chunk` packed tokens of one unit,
-// each of its 4 waves a quarter of them; the last split of a unit is its
-// fp16 residual when it has one.  A wave computes all its logits (phase K),
-// its softmax statistics, then P.V (phase V); the block merges its waves in
-// LDS and writes one partial (max, sum, unnormalised o) to the workspace.
+// each of its waves (4, or 12 in the one-round GQA form) an equal share;
+// the fp16 residual runs on the idle waves of the unit's last packed split,
+// or on a split of its own when those are too few.  A wave computes all its
+// logits (phase K), its softmax statistics, then P.V (phase V); the block
+// merges its waves in LDS and writes one partial (max, sum, unnormalised o)
+// to the workspace.
 // A second kernel merges the partials of each (unit, head) and writes o.
 // Small calls (64 tokens per wave) use a form that requests all of a
 // wave's loads at once (ONE below); the persistence audit adds a third
 // kernel that turns stored logits into per-token attention mass.
 //
-// Fused append: when the caller passes a new token, the residual block reads
+// Fused append: when the caller passes a new token, the residual waves read
 // it from the call's input, uses it as residual slot `new_slot`, and stores
 // it there for later calls.
 #include <algorithm>
