@@ -447,6 +447,23 @@ def main():
     mass_call_ms = ka.elapsed_time(kb) / (R * L)
     dec_call_bytes = np.array([decode_bytes(c, x.n_packed, x.n_res)
                                for x in caches], np.float64)
+    # each layer's call on its own (a graph of R back-to-back calls of that
+    # layer between HIP events): the per-layer median and p90
+    layer_us = []
+    for l in range(L):
+        side.wait_stream(stream)
+        g_l = capture(lambda: [minikv.decode_attn(dims, caches[l],
+                                                  dq[0, l % nl], o=od,
+                                                  ws=ws_dec)
+                               for _ in range(R)], side)
+        stream.wait_stream(side)
+        g_l.replay()
+        ka.record(stream)
+        g_l.replay()
+        kb.record(stream)
+        torch.cuda.synchronize()
+        layer_us.append(ka.elapsed_time(kb) * 1e3 / R)
+        del g_l
     pre_call_ms = []
     for l in range(L):
         q, k, v = qkv[l % nl]
@@ -515,6 +532,10 @@ def main():
             "avg_launch_us": round(avg_dec_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": int(avg_dec_bytes),
             "launches": R * L,
+            "per_layer_call_us": {"median": round(float(np.median(layer_us)), 3),
+                                  "p90": round(float(np.percentile(layer_us, 90)), 3),
+                                  "min": round(min(layer_us), 3),
+                                  "max": round(max(layer_us), 3)},
         },
         "roofline_prefill": {
             "kernel": "minikv_prefill_select (pass 1 + pass 2 + select)",
