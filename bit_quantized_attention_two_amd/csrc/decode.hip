@@ -505,14 +505,10 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
 #pragma unroll
         for (int i = 0; i < 4; ++i) za[P][i] = 0.f;
     }
-    uint32_t vw[NPASS][MBP];
-    if constexpr (!ONE)
-#pragma unroll
-        for (int P = 0; P < NPASS; ++P) load_vw(P, 0, vw[P]);
     const int nsteps = nt32 >> 5;
-#pragma unroll(ONE ? NVE : 1)
-    for (int e = 0; e < (ONE ? NVE : nsteps); ++e) {
-        if (ONE && e >= nsteps) break;            // uniform
+    // one 32-token step of every pass; `code(P, mb)` gives the step's value
+    // word, `after(P)` runs once the pass's words are in code operands
+    auto step = [&](int e, auto &&code, auto &&after) {
         const int st = 32 * e;
         const float *pp = &L.ls[hc * kLsStride + st + tb];
         const float4_t p0 = *reinterpret_cast<const float4_t *>(pp);
@@ -521,17 +517,9 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         for (int P = 0; P < NPASS; ++P) {
             const int vg = P * GPP + r % GPP;
             half8_t av[MBP];
-            if constexpr (ONE) {
 #pragma unroll
-                for (int mb = 0; mb < MBP; ++mb)
-                    av[mb] = code_operand(vwe[P][e][mb] >> (8 * (qd & 1)));
-            } else {
-#pragma unroll
-                for (int mb = 0; mb < MBP; ++mb) av[mb] = code_operand(vw[P][mb] >> (8 * (qd & 1)));
-                __builtin_amdgcn_sched_barrier(0);
-                load_vw(P, min(st + 32, nt32 - 32), vw[P]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int mb = 0; mb < MBP; ++mb) av[mb] = code_operand(code(P, mb) >> (8 * (qd & 1)));
+            after(P);
             const half_t *sp = &L.sv[vg * kSvStride + st + tb];
             const half_t *zp = &L.zv[vg * kSvStride + st + tb];
             const half4_t s0 = *reinterpret_cast<const half4_t *>(sp);
@@ -557,6 +545,33 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                 outv[P][mb] = mfma16(av[mb], bh, outv[P][mb]);
                 outv[P][mb] = mfma16(av[mb], bl, outv[P][mb]);
             }
+        }
+    };
+    if constexpr (ONE) {
+#pragma unroll
+        for (int e = 0; e < NVE; ++e) {
+            if (e >= nsteps) break;               // uniform
+            step(e, [&](int P, int mb) { return vwe[P][e][mb]; }, [](int) {});
+        }
+    } else {
+        // value words two steps ahead: buffer A holds even steps, B odd
+        uint32_t vwA[NPASS][MBP], vwB[NPASS][MBP];
+#pragma unroll
+        for (int P = 0; P < NPASS; ++P) load_vw(P, 0, vwA[P]);
+#pragma unroll
+        for (int P = 0; P < NPASS; ++P) load_vw(P, min(32, nt32 - 32), vwB[P]);
+        for (int e = 0; e < nsteps; e += 2) {
+            step(e, [&](int P, int mb) { return vwA[P][mb]; }, [&](int P) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_vw(P, min(32 * (e + 2), nt32 - 32), vwA[P]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if (e + 1 < nsteps)                   // uniform
+                step(e + 1, [&](int P, int mb) { return vwB[P][mb]; }, [&](int P) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_vw(P, min(32 * (e + 3), nt32 - 32), vwB[P]);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
         }
     }
     float zsum[NPASS];
