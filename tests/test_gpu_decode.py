@@ -203,15 +203,16 @@ def test_decode_multi_batch_waves(D, g, Gv):
     _decode_and_compare(torch, mk, dims, cache, oc, q, units)
 
 
-@pytest.mark.parametrize("n,m", [(41000, 40000), (24000, 23400)])
-def test_decode_one_round_gqa(n, m):
+@pytest.mark.parametrize("n,m,D", [(41000, 40000, 128), (24000, 23400, 128),
+                                   (41000, 40000, 64)])
+def test_decode_one_round_gqa(n, m, D):
     """g = 4 calls in the one-round 12-wave form: 8 kv heads x 27 splits of
     1536 tokens (128 per wave; the 4-wave form would need 512-token splits)
-    and 8 kv heads x 31 splits of 768 tokens (64 per wave); every unit
-    against the oracle."""
+    and 8 kv heads x 31 splits of 768 tokens (64 per wave), at D = 128 and
+    64; every unit against the oracle."""
     torch, mk = require_gpu()
-    B, Hkv, g, D = 1, 8, 4, 128
-    say("decode-one-round-gqa", dict(n=n, m=m))
+    B, Hkv, g = 1, 8, 4
+    say("decode-one-round-gqa", dict(n=n, m=m, D=D))
     dims, cache, oc = _build(torch, mk, B, Hkv, g, D, 16, 16, n, m,
                              seed=90 + m % 7, check_bits=False)
     q, kn, vn = synth.gen_decode_step(9, 0, 0, B, Hkv * g, Hkv, D)
