@@ -203,17 +203,19 @@ def test_decode_multi_batch_waves(D, g, Gv):
     _decode_and_compare(torch, mk, dims, cache, oc, q, units)
 
 
-@pytest.mark.parametrize("n,m,D", [(41000, 40000, 128), (24000, 23400, 128),
-                                   (41000, 40000, 64)])
-def test_decode_one_round_gqa(n, m, D):
+@pytest.mark.parametrize("n,m,D,Gk,Gv", [
+    (41000, 40000, 128, 16, 16), (24000, 23400, 128, 16, 16),
+    (41000, 40000, 64, 16, 16), (41000, 40000, 128, 64, 32)])
+def test_decode_one_round_gqa(n, m, D, Gk, Gv):
     """g = 4 calls in the one-round 12-wave form: 8 kv heads x 27 splits of
     1536 tokens (128 per wave; the 4-wave form would need 512-token splits)
     and 8 kv heads x 31 splits of 768 tokens (64 per wave), at D = 128 and
-    64; every unit against the oracle."""
+    64, and with key groups of 64 tokens and value groups of 32 channels;
+    every unit against the oracle."""
     torch, mk = require_gpu()
     B, Hkv, g = 1, 8, 4
-    say("decode-one-round-gqa", dict(n=n, m=m, D=D))
-    dims, cache, oc = _build(torch, mk, B, Hkv, g, D, 16, 16, n, m,
+    say("decode-one-round-gqa", dict(n=n, m=m, D=D, Gk=Gk, Gv=Gv))
+    dims, cache, oc = _build(torch, mk, B, Hkv, g, D, Gk, Gv, n, m,
                              seed=90 + m % 7, check_bits=False)
     q, kn, vn = synth.gen_decode_step(9, 0, 0, B, Hkv * g, Hkv, D)
     mk.append(dims, cache, dev16(torch, kn), dev16(torch, vn))
