@@ -152,7 +152,9 @@ def layer_decode_roofline(stream, config_id=3):
     is latency-bound instead.  Two such caches alternate (more than the
     256 MB last-level cache at the 13B shape, so no call finds the previous
     call's data there), timed as a graph of back-to-back calls between HIP
-    events on `stream`; the median of 5 replays is reported."""
+    events on `stream`: 10 replays to warm up (the GPU's clock ramps up
+    under sustained load; single replays right after other work run ~15%
+    slower), then the median of 10 replays."""
     import torch
     from bit_quantized_attention_two_amd import configs, minikv
     c = configs.get(config_id)
@@ -191,9 +193,10 @@ def layer_decode_roofline(stream, config_id=3):
             for i in range(R):
                 minikv.decode_attn(dims, caches[i % 2], q, o=o, ws=ws)
     stream.wait_stream(side)
-    gr.replay()
+    for _ in range(10):                          # the clock ramps up under
+        gr.replay()                              # sustained load: warm up
     ev = [(torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+           torch.cuda.Event(enable_timing=True)) for _ in range(10)]
     for a, b in ev:
         a.record(stream)
         gr.replay()
