@@ -397,6 +397,13 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         wave_lds_sync();
     }
     float mloc = -INFINITY;
+    // g = 1 with 16-token key groups: the key operand's column T belongs to
+    // the wave's tile T, so each lane keeps the accumulator of its own
+    // column's tile (a select per tile) and the logit epilogue runs once
+    // after the key phase instead of once per tile on a sixteenth of the
+    // lanes.
+    const bool per_lane = G == 1 && Gk == 16;     // uniform
+    float4_t keep = {0.f, 0.f, 0.f, 0.f};
     for (int b = 0; b < nbatch; ++b) {
         const int tok = b * BT;                   // wave-relative
         const int nxt = min(tok + BT, last);      // next batch (clamped)
@@ -425,7 +432,9 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                 acc = mfma16(av, bhi[kb], acc);
                 acc = mfma16(av, blo[kb], acc);
             }
-            if (gcol == tl / Gk - gb && tok + 16 * j < nt) {
+            if (per_lane) {
+                if (tok + 16 * j < nt && gcol == tl / Gk - gb) keep = acc;
+            } else if (gcol == tl / Gk - gb && tok + 16 * j < nt) {
                 const float bz = L.bias[(tl / Gk - gb) * G + hk];
                 float4_t lg;
 #pragma unroll
@@ -445,6 +454,19 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             load_kwords(nxt);
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+    if (per_lane && 16 * gcol < nt) {             // this lane's tile: gcol
+        const float bz = L.bias[gcol * G + hk];
+        float4_t lg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lg[i] = __builtin_fmaf(keep[i], kfac, bz);
+            mloc = fmaxf(mloc, lg[i]);
+        }
+        *reinterpret_cast<float4_t *>(&L.ls[hk * kLsStride + 16 * gcol + 4 * qd]) = lg;
+        if constexpr (MASS)
+            *reinterpret_cast<float4_t *>(
+                a.lg + ((size_t)unit * G + hk) * a.lg_stride + t0 + 16 * gcol + 4 * qd) = lg;
     }
 
     // ================================================== softmax, staging
