@@ -382,6 +382,7 @@ int32_t minikv_pack(const minikv_dims *d, int32_t n, const void *k,
         src.src_unit = (size_t)n * d->head_dim;
         src.sel = sel;
         src.sel_unit = (size_t)n_sel;
+        src.n_rows = n;
         hipError_t e = minikv::launch_pack(src, d->batch * d->n_kv_heads, n_tok,
                                            n_tail, 0, view_of(d, c),
                                            static_cast<hipStream_t>(stream));
@@ -417,6 +418,7 @@ int32_t minikv_append(const minikv_dims *d, minikv_layer_cache *c,
         src.src_unit = cv.res_unit();
         src.sel = nullptr;
         src.sel_unit = 0;
+        src.n_rows = d->residual_cap;
         e = minikv::launch_pack(src, units, d->residual_cap, 0, c->n_packed, cv, s);
         if (e != hipSuccess) return hip_status(e, "flush launch");
         c->n_packed += d->residual_cap;
@@ -444,6 +446,20 @@ static int32_t check_decode(const minikv_dims *d, const minikv_layer_cache *c,
     return MINIKV_OK;
 }
 
+// The launch's own split plan, checked on the host before any HIP call (it
+// always fits a workspace sized for the capacity; checked all the same).
+static int32_t check_decode_plan(const minikv_dims *d, int32_t n_packed,
+                                 int32_t n_res, size_t ws_bytes, bool mass) {
+    const int units = d->batch * d->n_kv_heads;
+    const int g = d->n_q_heads / d->n_kv_heads;
+    const size_t need = minikv::decode_plan_ws_bytes(units, g, d->head_dim, n_packed,
+                                                     n_res, d->group_k, mass);
+    if (need == 0 || need > ws_bytes)
+        return fail(MINIKV_EINVAL, "decode split plan does not fit the workspace (%zu > %zu)",
+                    need, ws_bytes);
+    return MINIKV_OK;
+}
+
 int32_t minikv_decode_attn(const minikv_dims *d, const minikv_layer_cache *c,
                            const void *q, void *o, void *ws, size_t ws_bytes,
                            void *stream) {
@@ -451,6 +467,7 @@ int32_t minikv_decode_attn(const minikv_dims *d, const minikv_layer_cache *c,
     CHECK(check_cache(d, c));
     CHECK(check_decode(d, c, q, o, ws, ws_bytes));
     if (c->n_packed + c->n_res == 0) return fail(MINIKV_EINVAL, "cache holds no token");
+    CHECK(check_decode_plan(d, c->n_packed, c->n_res, ws_bytes, false));
     CHECK(check_device());
     const int units = d->batch * d->n_kv_heads;
     const int g = d->n_q_heads / d->n_kv_heads;
@@ -473,9 +490,14 @@ int32_t minikv_append_decode(const minikv_dims *d, minikv_layer_cache *c,
     const bool flush = c->n_res + 1 == d->residual_cap;
     if (flush) {
         // the residual is packed first: the separate calls, in order
+        if (c->n_packed + d->residual_cap > c->capacity)
+            return fail(MINIKV_ECAPACITY, "flush of %d tokens exceeds capacity %d",
+                        d->residual_cap, c->capacity);
+        CHECK(check_decode_plan(d, c->n_packed + d->residual_cap, 0, ws_bytes, false));
         CHECK(minikv_append(d, c, k_new, v_new, stream));
         return minikv_decode_attn(d, c, q, o, ws, ws_bytes, stream);
     }
+    CHECK(check_decode_plan(d, c->n_packed, c->n_res + 1, ws_bytes, false));
     CHECK(check_device());
     const int units = d->batch * d->n_kv_heads;
     const int g = d->n_q_heads / d->n_kv_heads;
@@ -508,6 +530,7 @@ int32_t minikv_decode_attn_mass(const minikv_dims *d, const minikv_layer_cache *
                                                      d->residual_cap);
     if (ws_bytes < need)
         return fail(MINIKV_EINVAL, "workspace too small: %zu < %zu", ws_bytes, need);
+    CHECK(check_decode_plan(d, c->n_packed, c->n_res, ws_bytes, true));
     CHECK(check_device());
     const minikv::MassOut mo{mass, mass_stride};
     return hip_status(minikv::launch_decode(static_cast<const uint16_t *>(q),

@@ -1066,6 +1066,46 @@ int decode_max_capacity(int g) {
     return (kMaxSplit - 1) * kMaxWaveChunk * kWaves;
 }
 
+// The split plan of one call: chunk size, waves per block, packed splits,
+// and where the residual runs.
+struct Plan {
+    int chunk, waves, n_chunks, nsplit, res_split, res_wave0;
+};
+
+static Plan make_plan(int units, int g, int n_packed, int n_res, int Gk, bool mass) {
+    Plan p;
+    p.chunk = pick_chunk(units, n_packed, Gk, g, mass);
+    p.waves = p.chunk % kBigWaves == 0 ? kBigWaves : kWaves;   // W = 4 chunks are 2^k
+    p.n_chunks = (n_packed + p.chunk - 1) / p.chunk;
+    p.nsplit = p.n_chunks;
+    p.res_split = -1;
+    p.res_wave0 = 0;
+    if (n_res > 0) {
+        // waves of 64 residual tokens at most; in the last packed split's
+        // idle waves when there are enough of them
+        const int W = p.waves;
+        const int wchunk = p.chunk / W;
+        const int need = (n_res + 63) / 64;
+        const int used = p.n_chunks > 0
+            ? (n_packed - (p.n_chunks - 1) * p.chunk + wchunk - 1) / wchunk : W;
+        if (W - used >= need) {
+            p.res_split = p.n_chunks - 1;
+            p.res_wave0 = W - need;
+        } else {
+            p.res_split = p.n_chunks;
+            p.nsplit = p.n_chunks + 1;
+        }
+    }
+    return p;
+}
+
+size_t decode_plan_ws_bytes(int units, int g, int D, int n_packed, int n_res, int Gk,
+                            bool mass) {
+    const Plan p = make_plan(units, g, n_packed, n_res, Gk, mass);
+    if (p.nsplit > kMaxSplit) return 0;
+    return part_bytes(units, g, D, p.nsplit);
+}
+
 hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
                          int n_packed, int n_res, const CacheView &c,
                          const uint16_t *k_new, const uint16_t *v_new,
@@ -1077,32 +1117,19 @@ hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
     a.c = c;
     a.n_packed = n_packed;
     a.n_res = n_res;
-    a.chunk = pick_chunk(units, n_packed, c.Gk, g, mo != nullptr);
-    a.waves = a.chunk % kBigWaves == 0 ? kBigWaves : kWaves;   // W = 4 chunks are 2^k
-    a.n_chunks = (n_packed + a.chunk - 1) / a.chunk;
-    a.nsplit = a.n_chunks;
-    a.res_split = -1;
-    a.res_wave0 = 0;
-    if (n_res > 0) {
-        // waves of 64 residual tokens at most; in the last packed split's
-        // idle waves when there are enough of them
-        const int W = a.waves;
-        const int wchunk = a.chunk / W;
-        const int need = (n_res + 63) / 64;
-        const int used = a.n_chunks > 0
-            ? (n_packed - (a.n_chunks - 1) * a.chunk + wchunk - 1) / wchunk : W;
-        if (W - used >= need) {
-            a.res_split = a.n_chunks - 1;
-            a.res_wave0 = W - need;
-        } else {
-            a.res_split = a.n_chunks;
-            a.nsplit = a.n_chunks + 1;
-        }
-    }
+    const Plan p = make_plan(units, g, n_packed, n_res, c.Gk, mo != nullptr);
+    a.chunk = p.chunk;
+    a.waves = p.waves;
+    a.n_chunks = p.n_chunks;
+    a.nsplit = p.nsplit;
+    a.res_split = p.res_split;
+    a.res_wave0 = p.res_wave0;
     a.qscale = kLog2e / sqrtf((float)c.D);
     a.k_new = k_new;
     a.v_new = v_new;
     a.new_slot = n_res - 1;
+    // the entry points check the plan against the workspace before any HIP
+    // call; this guard is never taken after that validation
     if (part_bytes(units, g, c.D, a.nsplit) > ws_bytes || a.nsplit > kMaxSplit)
         return hipErrorInvalidValue;
     a.part_ml = static_cast<float *>(ws);

@@ -26,11 +26,14 @@ struct CacheView {
 
 // Source rows for packing: row p of unit u is src[u*src_unit + r*D ...]
 // with r = sel ? sel[u*sel_unit + p] : p.
+// A selected index outside [0, n_rows) is clamped into it, so a bad index
+// never reads outside the unit's rows.
 struct PackSrc {
     const uint16_t *k, *v;
     size_t src_unit;        // elements between units
     const int32_t *sel;     // nullable: identity
     size_t sel_unit;
+    int n_rows;             // source rows per unit
 };
 
 // Quantise n_tok tokens (multiple of Gk) of every unit into the packed
@@ -47,6 +50,10 @@ hipError_t launch_append_copy(const uint16_t *k_new, const uint16_t *v_new,
 // Decode attention: q, o [units*g][D].  Caches up to decode_max_capacity(g)
 // packed tokens per unit.
 size_t decode_ws_bytes(int units, int g, int D, int capacity);
+// Workspace bytes the call's split plan needs (<= decode_ws_bytes of any
+// capacity >= n_packed), or 0 if the plan is not possible (too many splits).
+size_t decode_plan_ws_bytes(int units, int g, int D, int n_packed, int n_res,
+                            int Gk, bool mass);
 size_t decode_mass_ws_bytes(int units, int g, int D, int capacity, int nr);
 int decode_max_capacity(int g);
 // Persistence audit output: mass[unit * stride + t] += the attention weight

@@ -90,7 +90,9 @@ __global__ __launch_bounds__(256) void pack_keys_kernel(
     auto load_rows = [&](int t0) {
         int row[RB];
 #pragma unroll
-        for (int i = 0; i < RB; ++i) row[i] = sel ? sel[p0 + t0 + i] : p0 + t0 + i;
+        for (int i = 0; i < RB; ++i)
+            row[i] = sel ? (int)min((uint32_t)sel[p0 + t0 + i], (uint32_t)(src.n_rows - 1))
+                         : p0 + t0 + i;
 #pragma unroll
         for (int i = 0; i < RB; ++i)
             rr[i] = *reinterpret_cast<const uint4 *>(base + (size_t)row[i] * D);
@@ -170,7 +172,9 @@ __global__ __launch_bounds__(256) void pack_values_kernel(
         const int part = tidx % PER_ROW;
         if (slot >= n_tail) return;
         const int p = n_tok + slot;
-        const int row = src.sel ? src.sel[(size_t)unit * src.sel_unit + p] : p;
+        const int row = src.sel ? (int)min((uint32_t)src.sel[(size_t)unit * src.sel_unit + p],
+                                           (uint32_t)(src.n_rows - 1))
+                                : p;
         const size_t s_off = (size_t)unit * src.src_unit + (size_t)row * D;
         const size_t d_off = (size_t)unit * c.res_unit() + (size_t)slot * D;
         reinterpret_cast<uint4 *>(c.kres + d_off)[part] =
@@ -185,7 +189,9 @@ __global__ __launch_bounds__(256) void pack_values_kernel(
     const int G = bg % gpt;
     const int p = blk * 16 + e;
     if (p >= n_tok) return;                      // whole rows leave
-    const int row = src.sel ? src.sel[(size_t)unit * src.sel_unit + p] : p;
+    const int row = src.sel ? (int)min((uint32_t)src.sel[(size_t)unit * src.sel_unit + p],
+                                       (uint32_t)(src.n_rows - 1))
+                            : p;
     const uint4 *x4 = reinterpret_cast<const uint4 *>(
         src.v + (size_t)unit * src.src_unit + (size_t)row * D + G * Gv);
 

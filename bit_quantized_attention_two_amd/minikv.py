@@ -121,12 +121,40 @@ def _stream(stream):
     return _P(stream.cuda_stream)
 
 
+def _on_device(t):
+    return t.is_cuda
+
+
 def _need(t, dtype, shape, name):
-    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or \
-            not t.is_contiguous() or not t.is_cuda:
+    """Every tensor handed to the library -- inputs and caller-supplied
+    outputs alike -- must have exactly the dtype, shape and contiguity the
+    kernels read or write: the C ABI cannot see buffer sizes, so a wrong
+    output would be written out of bounds."""
+    if not hasattr(t, "dtype") or t.dtype != dtype or \
+            tuple(t.shape) != tuple(shape) or not t.is_contiguous() or \
+            not _on_device(t):
         raise ValueError("%s must be a contiguous CUDA %s tensor of shape %s "
-                         "(got %s %s)" % (name, dtype, tuple(shape), t.dtype,
-                                          tuple(t.shape)))
+                         "(got %s)" % (name, dtype, tuple(shape),
+                                       "%s %s" % (t.dtype, tuple(t.shape))
+                                       if hasattr(t, "dtype") else type(t)))
+
+
+def _out(t, dtype, shape, name, like):
+    """A caller-supplied output, checked, or a new one on like's device."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    _need(t, dtype, shape, name)
+    return t
+
+
+def _ws(t, nbytes, name="ws"):
+    """A caller-supplied workspace: contiguous device bytes, at least
+    nbytes (the library checks the size it is told against its need)."""
+    if not hasattr(t, "is_contiguous") or not t.is_contiguous() or \
+            not _on_device(t) or t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s must be a contiguous CUDA buffer of at least %d "
+                         "bytes" % (name, nbytes))
+    return t.numel() * t.element_size()
 
 
 def make_dims(B, Hq, Hkv, D, Gk=16, Gv=16, residual_cap=128):
@@ -235,11 +263,9 @@ def prefill_attn(dims, q, k, v, o=None, lse=None, col=None, stream=None):
     _need(q, torch.float16, (B, Hq, n, D), "q")
     _need(k, torch.float16, (B, Hkv, n, D), "k")
     _need(v, torch.float16, (B, Hkv, n, D), "v")
-    o = torch.empty_like(q) if o is None else o
-    lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device) \
-        if lse is None else lse
-    col = torch.empty((B, Hkv, n), dtype=torch.float32, device=q.device) \
-        if col is None else col
+    o = _out(o, torch.float16, (B, Hq, n, D), "o", q)
+    lse = _out(lse, torch.float32, (B, Hq, n), "lse", q)
+    col = _out(col, torch.float32, (B, Hkv, n), "col", q)
     _check(lib().minikv_prefill_attn(ctypes.byref(dims), n, _ptr(q), _ptr(k),
                                      _ptr(v), _ptr(o), _ptr(lse), _ptr(col),
                                      _stream(stream)))
@@ -250,8 +276,7 @@ def select(dims, col, n_hh, n_recent, sel=None, stream=None):
     B, Hkv = dims.batch, dims.n_kv_heads
     n = col.shape[-1]
     _need(col, torch.float32, (B, Hkv, n), "col")
-    sel = torch.empty((B, Hkv, n_hh + n_recent), dtype=torch.int32,
-                      device=col.device) if sel is None else sel
+    sel = _out(sel, torch.int32, (B, Hkv, n_hh + n_recent), "sel", col)
     _check(lib().minikv_select(ctypes.byref(dims), n, _ptr(col), n_hh,
                                n_recent, _ptr(sel), _stream(stream)))
     return sel
@@ -264,17 +289,17 @@ def prefill_select(dims, q, k, v, n_hh, n_recent, o=None, col=None, lse=None,
     _need(q, torch.float16, (B, Hq, n, D), "q")
     _need(k, torch.float16, (B, Hkv, n, D), "k")
     _need(v, torch.float16, (B, Hkv, n, D), "v")
-    o = torch.empty_like(q) if o is None else o
-    col = torch.empty((B, Hkv, n), dtype=torch.float32, device=q.device) \
-        if col is None else col
-    sel = torch.empty((B, Hkv, n_hh + n_recent), dtype=torch.int32,
-                      device=q.device) if sel is None else sel
+    o = _out(o, torch.float16, (B, Hq, n, D), "o", q)
+    col = _out(col, torch.float32, (B, Hkv, n), "col", q)
+    sel = _out(sel, torch.int32, (B, Hkv, n_hh + n_recent), "sel", q)
+    if lse is not None:
+        _need(lse, torch.float32, (B, Hq, n), "lse")
     ws_bytes = 0
     if lse is None and ws is None:
         ws = torch.empty(prefill_ws_bytes(dims, n), dtype=torch.uint8,
                          device=q.device)
     if ws is not None:
-        ws_bytes = ws.numel() * ws.element_size()
+        ws_bytes = _ws(ws, 0 if lse is not None else prefill_ws_bytes(dims, n))
     _check(lib().minikv_prefill_select(
         ctypes.byref(dims), n, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(col),
         _ptr(lse), n_hh, n_recent, _ptr(sel), _ptr(ws), ws_bytes,
@@ -316,29 +341,30 @@ def decode_attn_mass(dims, cache, q, mass, o=None, ws=None, stream=None):
     shape = (dims.batch, dims.n_q_heads, dims.head_dim)
     _need(q, torch.float16, shape, "q")
     if (mass.dtype != torch.float32 or mass.dim() != 3 or not mass.is_contiguous()
+            or not _on_device(mass)
             or tuple(mass.shape[:2]) != (dims.batch, dims.n_kv_heads)):
         raise ValueError("mass: contiguous fp32 [B][Hkv][stride] expected")
-    o = torch.empty_like(q) if o is None else o
+    o = _out(o, torch.float16, shape, "o", q)
+    need = decode_mass_ws_bytes(dims, cache.capacity)
     if ws is None:
-        ws = torch.empty(decode_mass_ws_bytes(dims, cache.capacity),
-                         dtype=torch.uint8, device=q.device)
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = _ws(ws, need)
     _check(lib().minikv_decode_attn_mass(
         ctypes.byref(dims), ctypes.byref(cache.c), _ptr(q), _ptr(o),
-        _ptr(mass), mass.shape[2], _ptr(ws), ws.numel() * ws.element_size(),
-        _stream(stream)))
+        _ptr(mass), mass.shape[2], _ptr(ws), ws_bytes, _stream(stream)))
     return o
 
 
 def decode_attn(dims, cache, q, o=None, ws=None, stream=None):
     shape = (dims.batch, dims.n_q_heads, dims.head_dim)
     _need(q, torch.float16, shape, "q")
-    o = torch.empty_like(q) if o is None else o
+    o = _out(o, torch.float16, shape, "o", q)
+    need = decode_ws_bytes(dims, cache.capacity)
     if ws is None:
-        ws = torch.empty(decode_ws_bytes(dims, cache.capacity),
-                         dtype=torch.uint8, device=q.device)
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = _ws(ws, need)
     _check(lib().minikv_decode_attn(ctypes.byref(dims), ctypes.byref(cache.c),
-                                    _ptr(q), _ptr(o), _ptr(ws),
-                                    ws.numel() * ws.element_size(),
+                                    _ptr(q), _ptr(o), _ptr(ws), ws_bytes,
                                     _stream(stream)))
     return o
 
@@ -349,12 +375,14 @@ def append_decode(dims, cache, k_new, v_new, q, o=None, ws=None, stream=None):
     _need(k_new, torch.float16, kshape, "k_new")
     _need(v_new, torch.float16, kshape, "v_new")
     _need(q, torch.float16, (dims.batch, dims.n_q_heads, dims.head_dim), "q")
-    o = torch.empty_like(q) if o is None else o
+    o = _out(o, torch.float16, (dims.batch, dims.n_q_heads, dims.head_dim),
+             "o", q)
+    need = decode_ws_bytes(dims, cache.capacity)
     if ws is None:
-        ws = torch.empty(decode_ws_bytes(dims, cache.capacity),
-                         dtype=torch.uint8, device=q.device)
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = _ws(ws, need)
     _check(lib().minikv_append_decode(
         ctypes.byref(dims), ctypes.byref(cache.c), _ptr(k_new), _ptr(v_new),
-        _ptr(q), _ptr(o), _ptr(ws), ws.numel() * ws.element_size(),
-        _stream(stream)))
+        _ptr(q), _ptr(o), _ptr(ws), ws_bytes, _stream(stream)))
     return o
+

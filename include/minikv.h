@@ -206,7 +206,11 @@ MINIKV_API int32_t minikv_prefill_select(const minikv_dims *dims, int32_t n,
  * review of MiniKV, "Assumptions": group size 16 for per-channel keys and
  * per-token values; verdict record key_machinery: 16 codes per int32, fp16
  * scale and zero).
- *   k, v fp16 [B][Hkv][n][D]; sel int32 [B][Hkv][n_sel], ascending, < n.
+ *   k, v fp16 [B][Hkv][n][D]; sel int32 [B][Hkv][n_sel], ascending, in
+ *   [0, n).  The kernels clamp every index into [0, n) before reading a row
+ *   (a negative index reads row n - 1), so a bad index never reads outside
+ *   the unit's rows of k and v; the result for such an index is not
+ *   meaningful and is not diagnosed (the indices live in device memory).
  * The first floor(n_sel/Gk)*Gk selected tokens are packed (in the order of
  * sel); the remaining n_sel mod Gk are copied to the fp16 residual.  Sets
  * n_packed and n_res.  Codec per group x_1..x_G (fp32 arithmetic, RNE):
@@ -222,7 +226,10 @@ MINIKV_API int32_t minikv_pack(const minikv_dims *dims, int32_t n, const void *k
  * residual then holds residual_cap tokens they are packed as above onto the
  * end of the packed region and the residual is emptied.
  *   k_new, v_new fp16 [B][Hkv][D].
- * ECAPACITY, with no side effect, if that flush would exceed capacity. */
+ * ECAPACITY, with no side effect, if that flush would exceed capacity.
+ * EHIP if a launch fails: the host counters are then unchanged, and what
+ * the launches before it enqueued wrote only residual slot n_res and packed
+ * tokens past n_packed, i.e. outside the cache's valid contents. */
 MINIKV_API int32_t minikv_append(const minikv_dims *dims, minikv_layer_cache *cache,
                       const void *k_new, const void *v_new, void *stream);
 
@@ -235,7 +242,8 @@ MINIKV_API int32_t minikv_append(const minikv_dims *dims, minikv_layer_cache *ca
  * ws: at least minikv_decode_ws_bytes(dims, capacity) bytes of scratch for
  *   the split partial results; calls that share a workspace must not overlap
  *   in time.
- * EINVAL if the cache holds no token; EUNSUPPORTED if capacity exceeds
+ * EINVAL if the cache holds no token or the workspace is too small (both
+ * checked on the host, before any launch); EUNSUPPORTED if capacity exceeds
  * 511 * 1024 packed tokens. */
 MINIKV_API int32_t minikv_decode_attn(const minikv_dims *dims,
                            const minikv_layer_cache *cache, const void *q,

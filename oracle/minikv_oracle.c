@@ -165,10 +165,11 @@ float oracle_dequant(int code, uint16_t scale, uint16_t zero)
 /* ------------------------------------------------------------------------ */
 /* Per-layer budgets.                                                       */
 /*                                                                          */
-/* [R] "Assumptions & free parameters": cache budget 50% of prompt tokens,  */
-/* 25% heavy hitters + 25% recent window per layer; pyramid depth d = 7     */
-/* controls the linear interpolation of heavy-hitter budgets across layers, */
-/* with more budget in lower layers ("Core claim").                         */
+/* [R] "Assumptions & free parameters": half of the prompt is kept, a      */
+/* quarter as heavy hitters and a quarter as the most recent tokens, in     */
+/* every layer; a depth parameter (d = 7) sets how the heavy-hitter budget  */
+/* is spread linearly over the layers, the lower layers getting more        */
+/* ("Core claim").                                                          */
 /* reading: r = floor(n * rw_num / rw_den), k = floor(n * hh_num / hh_den); */
 /*   pyramid: k_min = floor(k / d), k_max = 2k - k_min, and layer l gets    */
 /*   k_min + floor((k_max - k_min) * (L-1-l) / (L-1)) (L = 1: k), clamped   */

@@ -77,3 +77,15 @@ def assert_cache_equal(gpu_cache, ocache, B, Hkv):
                                  "oracle=%r" % (name, len(idx), idx[0],
                                                 ga[tuple(idx[0])],
                                                 oa[tuple(idx[0])]))
+
+
+def lib_budgets(mk, c, n=None, n_layers=None):
+    """The library's per-layer budgets (minikv_pyramid_budgets) for workload
+    c, asserted equal to the oracle's before use."""
+    import oracle
+    n = c["n"] if n is None else n
+    L = c["L"] if n_layers is None else n_layers
+    ks, r = mk.pyramid_budgets(n, L, c["hh"], c["rw"], c["depth"], c["pyramid"])
+    oks, orr = oracle.budgets(n, L, c["depth"], c["pyramid"], c["hh"], c["rw"])
+    assert r == orr and list(ks) == list(oks), "library budgets differ from the oracle's"
+    return np.asarray(ks, np.int32), r

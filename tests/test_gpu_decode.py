@@ -8,7 +8,8 @@ import pytest
 
 import oracle
 from bit_quantized_attention_two_amd import synth
-from gpu_util import assert_cache_equal, assert_close, dev16, require_gpu, say
+from gpu_util import (assert_cache_equal, assert_close, dev16, lib_budgets,
+                      require_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -156,7 +157,7 @@ def test_decode_full_size(cfg_id):
     from bit_quantized_attention_two_amd import configs
     c = configs.get(cfg_id)
     B, Hkv, g, D, n = c["B"], c["Hkv"], c["g"], c["D"], c["n"]
-    ks, r = oracle.budgets(n, c["L"], c["depth"], c["pyramid"])
+    ks, r = lib_budgets(mk, c)
     m = int(ks[0]) + r
     say("decode-full", dict(cfg=cfg_id, B=B, Hkv=Hkv, g=g, n=n, m=m))
     units = [(b, h) for b in range(B) for h in range(Hkv)]

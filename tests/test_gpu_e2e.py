@@ -18,7 +18,7 @@ import pytest
 import oracle
 from bit_quantized_attention_two_amd import configs, synth
 from gpu_util import (ATOL, RTOL, assert_close, cache_to_numpy, dev16,
-                      require_gpu, say)
+                      lib_budgets, require_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def test_pipeline(cfg_id, layer):
     c = configs.get(cfg_id)
     B, Hq, Hkv, D, n, g = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"], c["g"]
     Gk, Gv, nr = c["Gk"], c["Gv"], c["residual_cap"]
-    ks, r = oracle.budgets(n, c["L"], c["depth"], c["pyramid"])
+    ks, r = lib_budgets(mk, c)
     n_hh = int(ks[layer])
     steps = c["decode_steps"]
     q, k, v = synth.gen_prefill(cfg_id, layer)
@@ -124,7 +124,7 @@ def test_persistence_reselection(cfg_id):
     torch, mk = require_gpu()
     c = configs.get(cfg_id)
     B, Hq, Hkv, D, n, g = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"], c["g"]
-    ks, r = oracle.budgets(n, c["L"], c["depth"], c["pyramid"])
+    ks, r = lib_budgets(mk, c)
     n_hh = int(ks[0])
     S = c["decode_steps"]
     q, k, v = synth.gen_prefill(cfg_id, 0)

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from bit_quantized_attention_two_amd import synth
-from gpu_util import assert_cache_equal, dev16, require_gpu, say
+from gpu_util import assert_cache_equal, dev16, lib_budgets, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -144,7 +144,8 @@ def test_pack_full_size_llama2_7b_layers():
     (pyramid layer 0 and layer 31), every unit compared."""
     torch, mk = require_gpu()
     n, H, D = 4096, 32, 128
-    ks, r = oracle.budgets(n, 32, depth=7, pyramid=True)
+    from bit_quantized_attention_two_amd import configs
+    ks, r = lib_budgets(mk, configs.get(2))
     for layer in (0, 31):
         m = int(ks[layer]) + r
         _pack_case(torch, mk, 1, H, D, 16, 16, n, m, seed=layer,
