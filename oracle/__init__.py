@@ -11,4 +11,6 @@ from .build_oracle import build, lib_path  # noqa: F401
 from .api import (  # noqa: F401
     h2d, f2h_rne, quant_group, dequant, budgets, prefill_rows, prefill_unit,
     select, pack_unit, decode_unit, cache_bytes, OracleCache,
+    quant_group_bits, pack_unit_bits, dequant_unit, attend, complement,
+    diffkv_score, diffkv_tiers, OracleMixedCache,
 )

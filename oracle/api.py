@@ -46,6 +46,20 @@ def _load():
         lib.oracle_cache_bytes.argtypes = [i32, i32, i32, i32, i32,
                                            ctypes.c_double, i32, i32, P]
         lib.oracle_cache_bytes.restype = ctypes.c_double
+        lib.oracle_quant_group_bits.argtypes = [P, i32, ctypes.c_long, i32,
+                                                P, P, P]
+        lib.oracle_quant_group_bits.restype = None
+        lib.oracle_pack_unit_bits.argtypes = [i32] * 5 + [P, P, P, i32] + [P] * 8
+        lib.oracle_pack_unit_bits.restype = i32
+        lib.oracle_dequant_unit.argtypes = [i32] * 7 + [P] * 8
+        lib.oracle_dequant_unit.restype = i32
+        lib.oracle_attend.argtypes = [i32, i32, P, i32, P, P, P]
+        lib.oracle_attend.restype = i32
+        lib.oracle_diffkv_score.argtypes = [i32, i32, P, P]
+        lib.oracle_diffkv_score.restype = None
+        lib.oracle_diffkv_tiers.argtypes = [i32, P, ctypes.c_double,
+                                            ctypes.c_double, i32, P, P, P]
+        lib.oracle_diffkv_tiers.restype = i32
         _lib = lib
     return _lib
 
@@ -310,3 +324,213 @@ class OracleCache:
                            self.vq[b, h], self.vs[b, h], self.vz[b, h],
                            self.n_res, self.kres[b, h], self.vres[b, h],
                            with_mass)
+
+
+# --------------------------------------------------- mixed-precision caches --
+# MiKV ("Don't Discard, but Keep It Small": important tokens at high
+# precision, the others kept at low precision, regrouped by precision) and
+# DiffKV (K8V4 / K4V2 / pruned tiers by significance, decided per head).
+
+def quant_group_bits(x, bits):
+    """One b-bit group: (codes uint8[G], scale bits, zero bits)."""
+    x = _u16(x).ravel()
+    codes = np.zeros(x.size, np.uint8)
+    s = np.zeros(1, np.uint16)
+    z = np.zeros(1, np.uint16)
+    _load().oracle_quant_group_bits(_ptr(x), x.size, 1, int(bits), _ptr(codes),
+                                    _ptr(s), _ptr(z))
+    return codes, int(s[0]), int(z[0])
+
+
+def pack_unit_bits(k, v, sel, Gk, Gv, key_bits, value_bits):
+    """Pack one unit at key_bits / value_bits (bit planes of the INT2 word
+    layout).  Returns dict kq [Pk][mp][D/16], ks, kz [mp/Gk][D],
+    vq [Pv][mp/16][D], vs, vz [mp][D/Gv], kres, vres [m - mp][D]."""
+    k, v = _u16(k), _u16(v)
+    n, D = k.shape
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    m = sel.size
+    mp = (m // Gk) * Gk
+    out = dict(
+        kq=np.zeros((key_bits // 2, mp, D // 16), np.uint32),
+        ks=np.zeros((mp // Gk, D), np.uint16),
+        kz=np.zeros((mp // Gk, D), np.uint16),
+        vq=np.zeros((value_bits // 2, mp // 16, D), np.uint32),
+        vs=np.zeros((mp, D // Gv), np.uint16),
+        vz=np.zeros((mp, D // Gv), np.uint16),
+        kres=np.zeros((m - mp, D), np.uint16),
+        vres=np.zeros((m - mp, D), np.uint16),
+    )
+    rc = _load().oracle_pack_unit_bits(
+        D, Gk, Gv, key_bits, value_bits, _ptr(k), _ptr(v), _ptr(sel), m,
+        *[_ptr(out[x]) for x in ("kq", "ks", "kz", "vq", "vs", "vz",
+                                  "kres", "vres")])
+    if rc != mp:
+        raise ValueError("bad pack arguments")
+    return out
+
+
+def dequant_unit(Gk, Gv, key_bits, value_bits, n_packed, kq, ks, kz, vq, vs,
+                 vz):
+    """Dequantised K, V [n_packed][D] (fp32 values in fp64) of one unit's
+    segment; kq [Pk][cap][D/16], vq [Pv][cap/16][D], metadata for cap."""
+    kq, vq = np.ascontiguousarray(kq), np.ascontiguousarray(vq)
+    ks, kz, vs, vz = (np.ascontiguousarray(a) for a in (ks, kz, vs, vz))
+    cap, D = kq.shape[1], kq.shape[2] * 16
+    kh = np.zeros((max(n_packed, 1), D), np.float64)
+    vh = np.zeros_like(kh)
+    rc = _load().oracle_dequant_unit(D, Gk, Gv, key_bits, value_bits, n_packed,
+                                     cap, _ptr(kq), _ptr(ks), _ptr(kz),
+                                     _ptr(vq), _ptr(vs), _ptr(vz), _ptr(kh),
+                                     _ptr(vh))
+    if rc != 0:
+        raise ValueError("bad dequant arguments")
+    return kh[:n_packed], vh[:n_packed]
+
+
+def attend(q, kh, vh):
+    """Softmax attention of q [g][D] (fp16) over rows kh, vh [T][D] (fp64)."""
+    q = _u16(q)
+    g, D = q.shape
+    kh = np.ascontiguousarray(kh, np.float64)
+    vh = np.ascontiguousarray(vh, np.float64)
+    o = np.zeros((g, D), np.float64)
+    rc = _load().oracle_attend(D, g, _ptr(q), kh.shape[0], _ptr(kh), _ptr(vh),
+                               _ptr(o))
+    if rc != 0:
+        raise ValueError("bad attend arguments")
+    return o
+
+
+def complement(sel, n):
+    """The tokens of [0, n) not in sel, ascending: MiKV's low-precision
+    group (the tokens an eviction method would drop)."""
+    keep = np.ones(n, bool)
+    keep[np.asarray(sel, np.int64)] = False
+    return np.nonzero(keep)[0].astype(np.int32)
+
+
+def diffkv_score(col_h):
+    """col_h [g][n] per-head column sums -> significance [n] (average
+    received attention, max over the group's heads)."""
+    col_h = np.ascontiguousarray(col_h, np.float64)
+    g, n = col_h.shape
+    score = np.zeros(n, np.float64)
+    _load().oracle_diffkv_score(n, g, _ptr(col_h), _ptr(score))
+    return score
+
+
+def diffkv_tiers(score, thr_hi, thr_lo, Gk):
+    """(high tier, low tier) index arrays, ascending, from significance
+    scores and the two thresholds."""
+    score = np.ascontiguousarray(score, np.float64)
+    n = score.size
+    hi = np.zeros(max(n, 1), np.int32)
+    lo = np.zeros(max(n, 1), np.int32)
+    cnt = np.zeros(2, np.int32)
+    rc = _load().oracle_diffkv_tiers(n, _ptr(score), float(thr_hi),
+                                     float(thr_lo), Gk, _ptr(hi), _ptr(lo),
+                                     _ptr(cnt))
+    if rc != 0:
+        raise ValueError("bad tier arguments")
+    return hi[:cnt[0]], lo[:cnt[1]]
+
+
+class OracleMixedCache:
+    """One layer's mixed-precision cache for B x Hkv units: packed segments
+    of given key/value bits (each unit may hold its own count of packed
+    tokens in a segment) plus one fp16 residual.  Segment arrays:
+
+      kq [B][Hkv][Pk][cap][D/16], ks, kz [B][Hkv][cap/Gk][D]
+      vq [B][Hkv][Pv][cap/16][D], vs, vz [B][Hkv][cap][D/Gv]
+      n  [B][Hkv]   packed tokens per unit (multiples of Gk)
+
+    A residual flush quantises the residual into segment `flush_seg`."""
+
+    def __init__(self, B, Hkv, D, Gk, Gv, segs, residual_cap=128, flush_seg=0):
+        self.B, self.Hkv, self.D, self.Gk, self.Gv = B, Hkv, D, Gk, Gv
+        self.nr, self.flush_seg = residual_cap, flush_seg
+        self.segs = []
+        for kb, vb, cap in segs:
+            assert cap % Gk == 0 and cap % 16 == 0
+            self.segs.append(dict(
+                kbits=kb, vbits=vb, cap=cap,
+                kq=np.zeros((B, Hkv, kb // 2, cap, D // 16), np.uint32),
+                ks=np.zeros((B, Hkv, cap // Gk, D), np.uint16),
+                kz=np.zeros((B, Hkv, cap // Gk, D), np.uint16),
+                vq=np.zeros((B, Hkv, vb // 2, cap // 16, D), np.uint32),
+                vs=np.zeros((B, Hkv, cap, D // Gv), np.uint16),
+                vz=np.zeros((B, Hkv, cap, D // Gv), np.uint16),
+                n=np.zeros((B, Hkv), np.int64)))
+        self.kres = np.zeros((B, Hkv, residual_cap, D), np.uint16)
+        self.vres = np.zeros_like(self.kres)
+        self.n_res = 0
+
+    def _store(self, si, b, h, at, out):
+        S, Gk = self.segs[si], self.Gk
+        mp = out["kq"].shape[1]
+        if at + mp > S["cap"]:
+            raise ValueError("capacity exceeded")
+        S["kq"][b, h, :, at:at + mp] = out["kq"]
+        S["ks"][b, h, at // Gk:(at + mp) // Gk] = out["ks"]
+        S["kz"][b, h, at // Gk:(at + mp) // Gk] = out["kz"]
+        S["vq"][b, h, :, at // 16:(at + mp) // 16] = out["vq"]
+        S["vs"][b, h, at:at + mp] = out["vs"]
+        S["vz"][b, h, at:at + mp] = out["vz"]
+        S["n"][b, h] = at + mp
+
+    def pack(self, si, k, v, b, h, idx, tail=True):
+        """Pack token indices idx (ascending) of unit (b, h) into segment si
+        (replacing its contents); with tail, the last len(idx) mod Gk go to
+        the end of the residual."""
+        S = self.segs[si]
+        out = pack_unit_bits(_u16(k)[b, h], _u16(v)[b, h], idx, self.Gk,
+                             self.Gv, S["kbits"], S["vbits"])
+        self._store(si, b, h, 0, out)
+        t = out["kres"].shape[0]
+        assert tail or t == 0
+        return out["kres"], out["vres"]
+
+    def set_residual(self, kres, vres):
+        """kres, vres [B][Hkv][t][D], the same t for every unit."""
+        t = kres.shape[2]
+        assert t < self.nr
+        self.kres[:, :, :t] = _u16(kres)
+        self.vres[:, :, :t] = _u16(vres)
+        self.n_res = t
+
+    def append(self, k_new, v_new):
+        k_new, v_new = _u16(k_new), _u16(v_new)
+        S = self.segs[self.flush_seg]
+        if self.n_res + 1 == self.nr and S["n"].max() + self.nr > S["cap"]:
+            raise ValueError("capacity exceeded")
+        self.kres[:, :, self.n_res] = k_new
+        self.vres[:, :, self.n_res] = v_new
+        self.n_res += 1
+        if self.n_res == self.nr:
+            ident = np.arange(self.nr, dtype=np.int32)
+            for b in range(self.B):
+                for h in range(self.Hkv):
+                    out = pack_unit_bits(self.kres[b, h], self.vres[b, h], ident,
+                                         self.Gk, self.Gv, S["kbits"],
+                                         S["vbits"])
+                    self._store(self.flush_seg, b, h, int(S["n"][b, h]), out)
+            self.n_res = 0
+
+    def decode_unit(self, qg, b, h):
+        """o [g][D] fp64: attention over every segment's packed tokens of
+        unit (b, h) and the residual (order does not matter)."""
+        ks_, vs_ = [], []
+        for S in self.segs:
+            kh, vh = dequant_unit(self.Gk, self.Gv, S["kbits"], S["vbits"],
+                                  int(S["n"][b, h]), S["kq"][b, h], S["ks"][b, h],
+                                  S["kz"][b, h], S["vq"][b, h], S["vs"][b, h],
+                                  S["vz"][b, h])
+            ks_.append(kh)
+            vs_.append(vh)
+        r = self.n_res
+        ks_.append(np.vectorize(h2d)(self.kres[b, h, :r]).reshape(r, self.D)
+                   if r else np.zeros((0, self.D)))
+        vs_.append(np.vectorize(h2d)(self.vres[b, h, :r]).reshape(r, self.D)
+                   if r else np.zeros((0, self.D)))
+        return attend(qg, np.concatenate(ks_), np.concatenate(vs_))

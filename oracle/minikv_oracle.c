@@ -518,3 +518,259 @@ double oracle_cache_bytes(int n_layers, int n_heads, int head_dim, int lprompt,
         *full_bytes = elems * (double)(lprompt + lgen) * 2.0;
     return elems * tokens * bits_per_elem / 8.0;
 }
+
+/* ======================================================================== */
+/* Mixed-precision caches: MiKV (important tokens at high precision, the    */
+/* rest kept at low precision instead of evicted) and DiffKV (keys with     */
+/* more bits than values; tiers K8V4 / K4V2 / pruned by significance).      */
+/*                                                                          */
+/* [M] "Don't Discard, but Keep It Small", rebuttal [W1] and the [UPDATED]  */
+/* implementation paragraph: evicted KVs are kept in low precision and      */
+/* important ones in high precision (an average of 3 bits between KIVI's 2  */
+/* and 4); the KV pairs are regrouped by precision, which attention allows  */
+/* because it does not depend on the order of the cached pairs, and each    */
+/* precision group is stored contiguously and attended with its own INTn x  */
+/* FP16 product.  The importance policy is H2O's cumulative score.          */
+/* [D] verdict record for arXiv 2412.03131, key_machinery / core_discovery: */
+/* significance = average attention a token receives from later tokens,   */
+/* max over the query heads of a GQA group, against thresholds alpha/N;     */
+/* above alpha_h/N keys 8 bits and values 4 bits, between alpha_l/N and     */
+/* alpha_h/N keys 4 and values 2, below alpha_l/N pruned; decided per head. */
+/* ======================================================================== */
+
+/* b-bit asymmetric codec (b = 2, 4 or 8) on one group.
+ * reading: as the INT2 codec with 2^b - 1 in place of 3: scale =
+ *   fp16((max - min) / (2^b - 1)) from one fp32 subtraction and one
+ *   correctly rounded fp32 division, zero = min (-0 -> +0), and the code is
+ *   the round-half-even of the exact d / scale (d = fp32(x - zero)) clamped
+ *   to [0, 2^b - 1]: the number of thresholds T_j = (j + 1/2) scale,
+ *   j = 0 .. 2^b - 2, that d exceeds, a tie d == T_j counting only for odd
+ *   j (then j + 1 is the even neighbour).  T_j is exact in fp32: j + 1/2 has
+ *   at most 9 significant bits and scale 11. */
+void oracle_quant_group_bits(const uint16_t *x, int G, long stride, int bits,
+                             uint8_t *codes, uint16_t *scale_out,
+                             uint16_t *zero_out)
+{
+    int top = (1 << bits) - 1;
+    float mn = (float)oracle_h2d(x[0]);
+    float mx = mn;
+    for (int i = 1; i < G; ++i) {
+        float xi = (float)oracle_h2d(x[(long)i * stride]);
+        if (xi < mn) mn = xi;
+        if (xi > mx) mx = xi;
+    }
+    float range = mx - mn;                        /* one fp32 rounding */
+    float s32 = range / (float)top;               /* one fp32 rounding */
+    uint16_t sh = oracle_f2h_rne(s32);
+    uint16_t zh = oracle_f2h_rne(mn + 0.0f);      /* exact: mn is a half */
+    float sf = (float)oracle_h2d(sh);
+    float zf = (float)oracle_h2d(zh);
+    *scale_out = sh;
+    *zero_out = zh;
+    for (int i = 0; i < G; ++i) {
+        if (sf == 0.0f) {
+            codes[i] = 0;
+            continue;
+        }
+        float d = (float)oracle_h2d(x[(long)i * stride]) - zf;
+        int c = 0;
+        for (int j = 0; j < top; ++j) {
+            float t = ((float)j + 0.5f) * sf;     /* exact */
+            if (d > t || (d == t && (j & 1)))
+                c = j + 1;
+        }
+        codes[i] = (uint8_t)c;
+    }
+}
+
+/* Pack one unit's selected tokens at key_bits / value_bits (2, 4 or 8; 2 or
+ * 4 for values).
+ * reading (bit planes): a b-bit code is stored as b/2 two-bit planes; plane
+ *   p holds bits 2p..2p+1 of every code, each plane in exactly the INT2
+ *   word layout (a key word: 16 channels of one token; a value word: 16
+ *   tokens of one channel; element e at bits 2e..2e+1).  The pages fix no
+ *   layout for 4- or 8-bit codes; planes keep one word format for every
+ *   precision.  Scales and zero-points as for INT2.
+ *   kq [key_bits/2][mp][D/16], vq [value_bits/2][mp/16][D] (plane-major),
+ *   ks, kz [mp/Gk][D], vs, vz [mp][D/Gv]; the last m mod Gk selected
+ *   tokens go to kres, vres [m - mp][D] as fp16.  Returns mp, -1 on bad
+ *   arguments. */
+int oracle_pack_unit_bits(int D, int Gk, int Gv, int key_bits, int value_bits,
+                          const uint16_t *k, const uint16_t *v,
+                          const int32_t *sel, int m, uint32_t *kq, uint16_t *ks,
+                          uint16_t *kz, uint32_t *vq, uint16_t *vs, uint16_t *vz,
+                          uint16_t *kres, uint16_t *vres)
+{
+    if (D % 16 || Gk % 16 || Gv % 16 || D % Gv || m < 0 || Gk <= 0 || Gv <= 0 ||
+        (key_bits != 2 && key_bits != 4 && key_bits != 8) ||
+        (value_bits != 2 && value_bits != 4))
+        return -1;
+    int mp = (m / Gk) * Gk;
+    int kp = key_bits / 2, vp = value_bits / 2;
+    long kplane = (long)mp * (D / 16), vplane = (long)(mp / 16) * D;
+    uint16_t *x = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(Gk > Gv ? Gk : Gv));
+    uint8_t *codes = (uint8_t *)malloc((size_t)(Gk > Gv ? Gk : Gv));
+
+    memset(kq, 0, sizeof(uint32_t) * (size_t)(kplane * kp));
+    for (int gi = 0; gi < mp / Gk; ++gi) {
+        for (int c = 0; c < D; ++c) {
+            for (int t = 0; t < Gk; ++t)
+                x[t] = k[(long)sel[gi * Gk + t] * D + c];
+            oracle_quant_group_bits(x, Gk, 1, key_bits, codes, &ks[(long)gi * D + c],
+                                    &kz[(long)gi * D + c]);
+            for (int t = 0; t < Gk; ++t) {
+                long p = (long)gi * Gk + t;
+                for (int pl = 0; pl < kp; ++pl)
+                    kq[pl * kplane + p * (D / 16) + c / 16] |=
+                        (uint32_t)((codes[t] >> (2 * pl)) & 3) << (2 * (c % 16));
+            }
+        }
+    }
+    memset(vq, 0, sizeof(uint32_t) * (size_t)(vplane * vp));
+    for (int p = 0; p < mp; ++p) {
+        const uint16_t *row = v + (long)sel[p] * D;
+        for (int G = 0; G < D / Gv; ++G) {
+            oracle_quant_group_bits(row + G * Gv, Gv, 1, value_bits, codes,
+                                    &vs[(long)p * (D / Gv) + G],
+                                    &vz[(long)p * (D / Gv) + G]);
+            for (int i = 0; i < Gv; ++i) {
+                int c = G * Gv + i;
+                for (int pl = 0; pl < vp; ++pl)
+                    vq[pl * vplane + (long)(p / 16) * D + c] |=
+                        (uint32_t)((codes[i] >> (2 * pl)) & 3) << (2 * (p % 16));
+            }
+        }
+    }
+    for (int p = mp; p < m; ++p) {
+        memcpy(kres + (long)(p - mp) * D, k + (long)sel[p] * D, sizeof(uint16_t) * D);
+        memcpy(vres + (long)(p - mp) * D, v + (long)sel[p] * D, sizeof(uint16_t) * D);
+    }
+    free(x);
+    free(codes);
+    return mp;
+}
+
+/* Dequantised keys and values of the first n_packed tokens of one unit's
+ * packed segment (layout of oracle_pack_unit_bits, with room for `cap`
+ * tokens: plane strides cap*D/16 and cap/16*D words), as fp32 values
+ * code * scale + zero stored in fp64 arrays kh, vh [n_packed][D]. */
+int oracle_dequant_unit(int D, int Gk, int Gv, int key_bits, int value_bits,
+                        int n_packed, int cap, const uint32_t *kq,
+                        const uint16_t *ks, const uint16_t *kz,
+                        const uint32_t *vq, const uint16_t *vs,
+                        const uint16_t *vz, double *kh, double *vh)
+{
+    if (n_packed < 0 || n_packed > cap || n_packed % Gk || cap % 16 || D % 16 ||
+        D % Gv)
+        return -1;
+    int kp = key_bits / 2, vp = value_bits / 2;
+    long kplane = (long)cap * (D / 16), vplane = (long)(cap / 16) * D;
+    for (int t = 0; t < n_packed; ++t) {
+        for (int c = 0; c < D; ++c) {
+            int kc = 0, vc = 0;
+            for (int pl = 0; pl < kp; ++pl)
+                kc |= (int)((kq[pl * kplane + (long)t * (D / 16) + c / 16] >>
+                             (2 * (c % 16))) & 3u) << (2 * pl);
+            for (int pl = 0; pl < vp; ++pl)
+                vc |= (int)((vq[pl * vplane + (long)(t / 16) * D + c] >>
+                             (2 * (t % 16))) & 3u) << (2 * pl);
+            long km = (long)(t / Gk) * D + c;
+            long vm = (long)t * (D / Gv) + c / Gv;
+            kh[(long)t * D + c] = (double)oracle_dequant(kc, ks[km], kz[km]);
+            vh[(long)t * D + c] = (double)oracle_dequant(vc, vs[vm], vz[vm]);
+        }
+    }
+    return 0;
+}
+
+/* Plain softmax attention of g query heads (fp16 q [g][D]) over T given key
+ * and value rows (fp64 [T][D]), scale 1/sqrt(D), fp64: o [g][D]. */
+int oracle_attend(int D, int g, const uint16_t *q, int T, const double *kh,
+                  const double *vh, double *o)
+{
+    if (T <= 0)
+        return -1;
+    double *s = (double *)malloc(sizeof(double) * (size_t)T);
+    const double scale = 1.0 / sqrt((double)D);
+    for (int h = 0; h < g; ++h) {
+        double M = -INFINITY;
+        for (int t = 0; t < T; ++t) {
+            double acc = 0.0;
+            for (int c = 0; c < D; ++c)
+                acc += oracle_h2d(q[(long)h * D + c]) * kh[(long)t * D + c];
+            s[t] = acc * scale;
+            if (s[t] > M) M = s[t];
+        }
+        double l = 0.0;
+        for (int t = 0; t < T; ++t) {
+            s[t] = exp(s[t] - M);
+            l += s[t];
+        }
+        for (int c = 0; c < D; ++c) {
+            double acc = 0.0;
+            for (int t = 0; t < T; ++t)
+                acc += s[t] * vh[(long)t * D + c];
+            o[(long)h * D + c] = acc / l;
+        }
+    }
+    free(s);
+    return 0;
+}
+
+/* DiffKV significance of every prompt token of one unit: the average of the
+ * attention it receives from the n - j causal rows i >= j, per query head,
+ * then the max over the g query heads of the group.
+ *   col_h [g][n]: per-head column sums (oracle_prefill_rows with g = 1).
+ *   score[j] = max_h col_h[h][j] / (n - j). */
+void oracle_diffkv_score(int n, int g, const double *col_h, double *score)
+{
+    for (int j = 0; j < n; ++j) {
+        double m = -INFINITY;
+        for (int h = 0; h < g; ++h)
+            if (col_h[(long)h * n + j] > m) m = col_h[(long)h * n + j];
+        score[j] = m / (double)(n - j);
+    }
+}
+
+/* DiffKV tiers of one unit from its significance scores.
+ * reading: cnt_hi = #{score > thr_hi}, cnt_kept = #{score > thr_lo}
+ *   (thr = alpha / n; the caller passes the thresholds); each count is
+ *   rounded up to a whole number of key groups (so every kept token sits in
+ *   a full group, none is left over), capped at floor(n / Gk) * Gk, with
+ *   kept >= hi.  The high tier is the first c_hi tokens in the order (score
+ *   descending, index ascending), the low tier the next c_kept - c_hi; the
+ *   rest are pruned.  Each tier is written in ascending index order.
+ *   counts[0] = c_hi, counts[1] = c_kept - c_hi.  Returns 0, -1 on bad
+ *   arguments. */
+int oracle_diffkv_tiers(int n, const double *score, double thr_hi,
+                        double thr_lo, int Gk, int32_t *hi, int32_t *lo,
+                        int32_t *counts)
+{
+    if (n < 0 || Gk <= 0)
+        return -1;
+    int cnt_hi = 0, cnt_kept = 0;
+    for (int j = 0; j < n; ++j) {
+        if (score[j] > thr_hi) ++cnt_hi;
+        if (score[j] > thr_lo) ++cnt_kept;
+    }
+    int cap = (n / Gk) * Gk;
+    int c_hi = (cnt_hi + Gk - 1) / Gk * Gk;
+    int c_kept = (cnt_kept + Gk - 1) / Gk * Gk;
+    if (c_hi > cap) c_hi = cap;
+    if (c_kept > cap) c_kept = cap;
+    if (c_kept < c_hi) c_kept = c_hi;
+    scored_t *cand = (scored_t *)malloc(sizeof(scored_t) * (size_t)(n > 0 ? n : 1));
+    for (int j = 0; j < n; ++j) {
+        cand[j].score = score[j];
+        cand[j].idx = j;
+    }
+    qsort(cand, (size_t)n, sizeof(scored_t), cmp_scored);
+    for (int t = 0; t < c_hi; ++t) hi[t] = cand[t].idx;
+    for (int t = c_hi; t < c_kept; ++t) lo[t - c_hi] = cand[t].idx;
+    qsort(hi, (size_t)c_hi, sizeof(int32_t), cmp_i32);
+    qsort(lo, (size_t)(c_kept - c_hi), sizeof(int32_t), cmp_i32);
+    counts[0] = c_hi;
+    counts[1] = c_kept - c_hi;
+    free(cand);
+    return 0;
+}
