@@ -120,3 +120,77 @@ def gen_kv(seed, units, n, D, outliers=True):
             ch = r.choice(D, min(N_OUTLIER_CH, D), replace=False)
             k[u][:, ch] *= OUTLIER_GAIN
     return k.astype(np.float16), v.astype(np.float16)
+
+
+# ------------------------------------------------ device-side generation --
+# The benchmark's full-size workloads (up to 51 GB of prompt tensors) are
+# drawn on the GPU with torch's counter-based generator instead of numpy's
+# PCG64, with the same recipe: N(0,1) fp32 draws, the sink and heavy-hitter
+# keys along the normalised mean query of the kv head's group, the same
+# outlier channels (numpy, tag 3) and planted positions (numpy, tag 4), and
+# one rounding to fp16.  Values differ from gen_prefill's; the structure and
+# distributions are the same.
+
+def _torch_gen(device, *key):
+    import torch
+    seed = int(rng(*key).integers(0, 2 ** 62))
+    return torch.Generator(device=device).manual_seed(seed)
+
+
+def gen_prefill_device(cfg_id, layer, device, c=None, structure=True):
+    """Q [B][Hq][n][D], K, V [B][Hkv][n][D] fp16 tensors on `device`."""
+    import torch
+    c = c or configs.get(cfg_id)
+    B, Hq, Hkv, n, D = c["B"], c["Hq"], c["Hkv"], c["n"], c["D"]
+    g = Hq // Hkv
+    r_window = n * c["rw"][0] // c["rw"][1]
+    q = torch.empty((B, Hq, n, D), dtype=torch.float16, device=device)
+    k = torch.empty((B, Hkv, n, D), dtype=torch.float16, device=device)
+    v = torch.empty_like(k)
+    och = outlier_channels(cfg_id, layer, Hkv, D)
+    for b in range(B):
+        gq = _torch_gen(device, cfg_id, layer, 0, b)
+        gk = _torch_gen(device, cfg_id, layer, 1, b)
+        gv = _torch_gen(device, cfg_id, layer, 2, b)
+        hr = rng(cfg_id, layer, 4, b)
+        for h in range(Hkv):
+            qf = torch.randn((g, n, D), generator=gq, device=device)
+            kf = torch.randn((n, D), generator=gk, device=device)
+            v[b, h] = torch.randn((n, D), generator=gv, device=device).half()
+            if structure and n > 0:
+                u = qf.double().mean(dim=(0, 1))
+                nu = torch.linalg.norm(u)
+                u = (u / nu if nu > 0 else
+                     torch.full((D,), D ** -0.5, dtype=torch.float64,
+                                device=device)).float()
+                kf[0] = SINK_GAIN * np.sqrt(D) * u
+                hi = max(n - r_window, 1)
+                cnt = min(N_HH_PLANTED, hi - 1)
+                if cnt > 0:
+                    pos = hr.choice(np.arange(1, hi), cnt, replace=False)
+                    kf[torch.from_numpy(pos).to(device)] = HH_GAIN * np.sqrt(D) * u
+                kf[:, torch.from_numpy(och[h]).to(device)] *= OUTLIER_GAIN
+            q[b, h * g:(h + 1) * g] = qf.half()
+            k[b, h] = kf.half()
+    return q, k, v
+
+
+def gen_decode_device(cfg_id, steps, layers, device, c=None):
+    """q [steps][layers][B][Hq][D], k, v [steps][layers][B][Hkv][D] fp16 on
+    `device`: N(0,1) draws with the layer's key outlier channels."""
+    import torch
+    c = c or configs.get(cfg_id)
+    B, Hq, Hkv, D = c["B"], c["Hq"], c["Hkv"], c["D"]
+    q = torch.empty((steps, layers, B, Hq, D), dtype=torch.float16, device=device)
+    k = torch.empty((steps, layers, B, Hkv, D), dtype=torch.float16, device=device)
+    v = torch.empty_like(k)
+    for l in range(layers):
+        gen = _torch_gen(device, cfg_id, l, 5, 0)
+        q[:, l] = torch.randn((steps, B, Hq, D), generator=gen, device=device).half()
+        kf = torch.randn((steps, B, Hkv, D), generator=gen, device=device)
+        och = outlier_channels(cfg_id, l, Hkv, D)
+        for h in range(Hkv):
+            kf[:, :, h][:, :, torch.from_numpy(och[h]).to(device)] *= OUTLIER_GAIN
+        k[:, l] = kf.half()
+        v[:, l] = torch.randn((steps, B, Hkv, D), generator=gen, device=device).half()
+    return q, k, v
