@@ -479,6 +479,37 @@ int32_t minikv_decode_attn(const minikv_dims *d, const minikv_layer_cache *c,
                       "decode launch");
 }
 
+int32_t minikv_decode_attn_noalloc(const minikv_dims *d, const minikv_layer_cache *c,
+                                   const void *q, void *o, void *stream) {
+    CHECK(check_dims(d));
+    CHECK(check_cache(d, c));
+    CHECK_PTR(q, "q");
+    CHECK_PTR(o, "o");
+    const int g = d->n_q_heads / d->n_kv_heads;
+    if (c->capacity > minikv::decode_max_capacity(g))
+        return fail(MINIKV_EUNSUPPORTED, "capacity %d above the decode limit %d",
+                    c->capacity, minikv::decode_max_capacity(g));
+    if (c->n_packed + c->n_res == 0) return fail(MINIKV_EINVAL, "cache holds no token");
+    const int units = d->batch * d->n_kv_heads;
+    const size_t need = minikv::decode_plan_ws_bytes(units, g, d->head_dim, c->n_packed,
+                                                     c->n_res, d->group_k, false);
+    if (need == 0 || need > minikv::kDecodeScratchBytes)
+        return fail(MINIKV_ECAPACITY,
+                    "split partials of this call (%zu bytes) exceed the %zu-byte "
+                    "scratch array; use minikv_decode_attn with a workspace",
+                    need, minikv::kDecodeScratchBytes);
+    CHECK(check_device());
+    void *ws = nullptr;
+    CHECK(hip_status(minikv::decode_scratch(&ws), "scratch address"));
+    return hip_status(minikv::launch_decode(static_cast<const uint16_t *>(q),
+                                            static_cast<uint16_t *>(o), units, g,
+                                            c->n_packed, c->n_res, view_of(d, c),
+                                            nullptr, nullptr, ws,
+                                            minikv::kDecodeScratchBytes,
+                                            static_cast<hipStream_t>(stream)),
+                      "decode launch");
+}
+
 int32_t minikv_append_decode(const minikv_dims *d, minikv_layer_cache *c,
                              const void *k_new, const void *v_new, const void *q,
                              void *o, void *ws, size_t ws_bytes, void *stream) {

@@ -45,6 +45,7 @@
 // it from the call's input, uses it as residual slot `new_slot`, and stores
 // it there for later calls.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -1059,6 +1060,37 @@ size_t decode_mass_ws_bytes(int units, int g, int D, int capacity, int nr) {
     return align256(decode_ws_bytes(units, g, D, capacity)) +
            align256((size_t)units * g * lg_stride_of(capacity, nr) * sizeof(float)) +
            (size_t)units * g * 2 * sizeof(float);
+}
+
+// ------------------------------------------------ allocation-free variant
+// A file-scope device array holds the split partials of
+// minikv_decode_attn_noalloc, for callers that cannot allocate.  Each GPU
+// holds its own copy until the process ends; in host code `scratch` is only a
+// stand-in for the symbol, so its device address is looked up once per device
+// (with that device current) and only that address is ever handed to a
+// kernel.  Every call on a GPU shares the array: calls that overlap on one
+// GPU race.  Nothing in it needs clearing: every split writes its partial
+// before the combine reads it.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[64];
+
+hipError_t decode_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 int decode_max_capacity(int g) {

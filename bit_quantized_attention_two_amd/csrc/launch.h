@@ -56,6 +56,11 @@ size_t decode_plan_ws_bytes(int units, int g, int D, int n_packed, int n_res,
                             int Gk, bool mass);
 size_t decode_mass_ws_bytes(int units, int g, int D, int capacity, int nr);
 int decode_max_capacity(int g);
+// Size of the device array that holds the split partials of the
+// allocation-free decode entry point, and its address on the current device
+// (looked up once per device).
+constexpr size_t kDecodeScratchBytes = 16u << 20;
+hipError_t decode_scratch(void **out);
 // Persistence audit output: mass[unit * stride + t] += the attention weight
 // of cache token t summed over the unit's g heads.
 struct MassOut {

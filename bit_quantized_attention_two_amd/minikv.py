@@ -84,6 +84,7 @@ def lib():
                                         _i32),
             "minikv_append_decode": ([D, C, _P, _P, _P, _P, _P, _sz, _P],
                                      _i32),
+            "minikv_decode_attn_noalloc": ([D, C, _P, _P, _P], _i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -99,7 +100,8 @@ EXPORTED = ("minikv_version", "minikv_status_str", "minikv_last_error",
             "minikv_decode_ws_bytes", "minikv_prefill_attn", "minikv_select",
             "minikv_prefill_select", "minikv_pack", "minikv_append",
             "minikv_decode_attn", "minikv_append_decode",
-            "minikv_decode_mass_ws_bytes", "minikv_decode_attn_mass")
+            "minikv_decode_mass_ws_bytes", "minikv_decode_attn_mass",
+            "minikv_decode_attn_noalloc")
 
 
 def status_str(s):
@@ -386,3 +388,14 @@ def append_decode(dims, cache, k_new, v_new, q, o=None, ws=None, stream=None):
         _ptr(q), _ptr(o), _ptr(ws), ws_bytes, _stream(stream)))
     return o
 
+
+def decode_attn_noalloc(dims, cache, q, o=None, stream=None):
+    """decode_attn without a workspace: the library's own per-device scratch
+    array holds the split partials (calls on one GPU must not overlap)."""
+    shape = (dims.batch, dims.n_q_heads, dims.head_dim)
+    _need(q, torch.float16, shape, "q")
+    o = _out(o, torch.float16, shape, "o", q)
+    _check(lib().minikv_decode_attn_noalloc(ctypes.byref(dims),
+                                            ctypes.byref(cache.c), _ptr(q),
+                                            _ptr(o), _stream(stream)))
+    return o

@@ -249,6 +249,21 @@ MINIKV_API int32_t minikv_decode_attn(const minikv_dims *dims,
                            const minikv_layer_cache *cache, const void *q,
                            void *o, void *ws, size_t ws_bytes, void *stream);
 
+/* minikv_decode_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments minus the workspace, same results bit for bit:
+ * the split partials go to a 16 MiB array that the library keeps in device
+ * memory on every GPU it runs on, until the process ends.  Every call on one
+ * GPU shares that array, so calls that overlap in time on one GPU (any
+ * streams) race and must be ordered by the caller.  No allocation, no
+ * memset.  ECAPACITY if the call's split partials would exceed 16 MiB
+ * (units * splits * g * (D + 2) * 4 bytes; e.g. 640 kv heads with 4096
+ * packed tokens need 1.7 MB); otherwise the errors of minikv_decode_attn. */
+MINIKV_API int32_t minikv_decode_attn_noalloc(const minikv_dims *dims,
+                                              const minikv_layer_cache *cache,
+                                              const void *q, void *o,
+                                              void *stream);
+
 /* minikv_append followed by minikv_decode_attn (the new token attends to
  * itself), with the same results bit for bit.  On a step that does not flush
  * the residual, the append happens inside the decode launch: the kernel reads

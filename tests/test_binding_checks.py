@@ -9,7 +9,8 @@ import torch
 
 COMPUTE = {"minikv_prefill_attn", "minikv_select", "minikv_prefill_select",
            "minikv_pack", "minikv_append", "minikv_decode_attn",
-           "minikv_append_decode", "minikv_decode_attn_mass"}
+           "minikv_append_decode", "minikv_decode_attn_mass",
+           "minikv_decode_attn_noalloc"}
 
 
 class Launched(Exception):
