@@ -89,3 +89,36 @@ def lib_budgets(mk, c, n=None, n_layers=None):
     oks, orr = oracle.budgets(n, L, c["depth"], c["pyramid"], c["hh"], c["rw"])
     assert r == orr and list(ks) == list(oks), "library budgets differ from the oracle's"
     return np.asarray(ks, np.int32), r
+
+
+def topk_of(col, n_hh, n_recent):
+    n = col.size
+    cand = np.arange(n - n_recent)
+    order = np.lexsort((cand, -col[:n - n_recent].astype(np.float64)))
+    return np.concatenate([np.sort(cand[order[:n_hh]]),
+                           np.arange(n - n_recent, n)]).astype(np.int32)
+
+
+def check_selection(gsel, gcol, osel, ocol, n_hh, n_recent):
+    """Selection protocol.  (1) The oracle's selection applied to the GPU's
+    own scores must be the GPU's selection exactly (the set is unique given
+    the scores, ties to the lower index).  (2) Against the oracle's
+    selection on its own scores, a difference is accepted only as swaps of
+    boundary candidates whose oracle scores agree with the k-th score within
+    the score tolerance.  Returns the number of swaps."""
+    import oracle
+    assert np.array_equal(gsel, oracle.select(np.asarray(gcol, np.float64),
+                                              n_hh, n_recent))
+    assert np.array_equal(gsel, topk_of(gcol, n_hh, n_recent))
+    if osel is None:
+        return 0
+    # (2) against the oracle's selection: only boundary swaps
+    if np.array_equal(gsel, osel):
+        return 0
+    a, b = set(gsel.tolist()), set(osel.tolist())
+    only_g, only_o = sorted(a - b), sorted(b - a)
+    assert len(only_g) == len(only_o)
+    kth = np.sort(ocol[:ocol.size - n_recent])[::-1][n_hh - 1]
+    for j in only_g + only_o:
+        assert abs(ocol[j] - kth) <= ATOL + RTOL * abs(kth), (j, ocol[j], kth)
+    return len(only_g)

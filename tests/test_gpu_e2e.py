@@ -17,33 +17,10 @@ import pytest
 
 import oracle
 from bit_quantized_attention_two_amd import configs, synth
-from gpu_util import (ATOL, RTOL, assert_close, cache_to_numpy, dev16,
-                      lib_budgets, require_gpu, say)
+from gpu_util import (assert_close, cache_to_numpy, check_selection as
+                      _check_selection, dev16, lib_budgets, require_gpu, say)
 
 pytestmark = pytest.mark.gpu
-
-
-def _topk_of(col, n_hh, n_recent):
-    n = col.size
-    cand = np.arange(n - n_recent)
-    order = np.lexsort((cand, -col[:n - n_recent].astype(np.float64)))
-    return np.concatenate([np.sort(cand[order[:n_hh]]),
-                           np.arange(n - n_recent, n)]).astype(np.int32)
-
-
-def _check_selection(gsel, gcol, osel, ocol, n_hh, n_recent):
-    # (1) unique given the GPU's scores
-    assert np.array_equal(gsel, _topk_of(gcol, n_hh, n_recent))
-    # (2) against the oracle's selection: only boundary swaps
-    if np.array_equal(gsel, osel):
-        return 0
-    a, b = set(gsel.tolist()), set(osel.tolist())
-    only_g, only_o = sorted(a - b), sorted(b - a)
-    assert len(only_g) == len(only_o)
-    kth = np.sort(ocol[:ocol.size - n_recent])[::-1][n_hh - 1]
-    for j in only_g + only_o:
-        assert abs(ocol[j] - kth) <= ATOL + RTOL * abs(kth), (j, ocol[j], kth)
-    return len(only_g)
 
 
 @pytest.mark.parametrize("cfg_id,layer", [(1, 0), (2, 0), (2, 31)])
