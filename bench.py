@@ -82,6 +82,12 @@ def parse():
                    help="skip the persistence audit (re-selection every 32 "
                         "decode steps, overlap with the prefill heavy "
                         "hitters)")
+    p.add_argument("--no-mixed", action="store_true",
+                   help="skip the MiKV / DiffKV mixed-precision records")
+    p.add_argument("--no-fused-tail", action="store_true",
+                   help="skip the fused prefill tail record")
+    p.add_argument("--mixed-configs", default="5,3",
+                   help="workloads of the mixed-precision records (layer 0)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="rough CPU budget of the oracle baseline")
     return p.parse_args()
@@ -169,15 +175,25 @@ def traffic_probe(config_id):
     k = torch.randn(B, Hkv, n, D, device="cuda", generator=g).half()
     v = torch.randn(B, Hkv, n, D, device="cuda", generator=g).half()
     kn = torch.randn(B, Hkv, D, device="cuda", generator=g).half()
+    nr, Gk = c["residual_cap"], c["Gk"]
     caches = []
     for l in range(L):
+        # the end-of-step state: the selection plus the decode steps'
+        # tokens, flushed every nr, packed directly (appends under the
+        # counters would each be a profiled dispatch); the residual's count
+        # is set on the host (its contents do not change the traffic)
         m = ks[l] + r
-        sel = (torch.arange(m, device="cuda", dtype=torch.int64) * n // m
-               ).int().repeat(B, Hkv, 1).contiguous()
+        n_res = m % Gk
+        n_packed = m - n_res
+        for _ in range(c["decode_steps"]):
+            n_res += 1
+            if n_res == nr:
+                n_packed, n_res = n_packed + nr, 0
+        sel = (torch.arange(n_packed, device="cuda", dtype=torch.int64) * n //
+               n_packed).int().repeat(B, Hkv, 1).contiguous()
         cache = minikv.LayerCache(dims, layer_capacity(c, m))
         minikv.pack(dims, k, v, sel, cache)
-        for _ in range(c["decode_steps"]):          # end-of-step state
-            minikv.append(dims, cache, kn, kn)
+        cache.c.n_res = n_res
         caches.append(cache)
     del k, v
     q = torch.randn(B, Hq, D, device="cuda", generator=g).half()
@@ -499,6 +515,221 @@ def run_workload(cfg_id, steps, warmup, args, stream, headline):
     return rec, state
 
 
+def mixed_decode_bytes(c, segs, n_res):
+    """Algorithmic bytes of one mixed-precision decode call: per unit and
+    segment, (key_bits + value_bits) D / 8 code bytes per packed token plus
+    fp16 scale and zero (per key group and channel, per token and value
+    group), the fp16 residual, and q and o.  segs: (key_bits, value_bits,
+    total packed tokens over all units)."""
+    D, Gk, Gv = c["D"], c["Gk"], c["Gv"]
+    total = 0
+    for kb, vb, tokens in segs:
+        total += tokens * (kb + vb) * D // 8 + (tokens // Gk) * D * 4 + \
+            tokens * (D // Gv) * 4
+    units = c["B"] * c["Hkv"]
+    return total + units * n_res * D * 4 + c["B"] * c["Hq"] * D * 4
+
+
+def mixed_records(stream, config_id, alphas=(1.0, 0.04)):
+    """MiKV and DiffKV at layer 0 of a workload, on its device-drawn inputs:
+      MiKV: the library's heavy-hitter + recent-window selection marks the
+        important tokens; minikv_pack_mikv keeps them at INT4 and every
+        other prompt token at INT2 (average 3 bits at a half/half split);
+      DiffKV: minikv_prefill_diffkv (pass 1 + the per-head significance
+        pass), minikv_tier_diffkv (alpha_hi, alpha_lo), minikv_pack_diffkv
+        (K8V4 / K4V2, per kv head).
+    Each then gets 64 decode-step tokens in the fp16 residual, and its
+    decode call is timed like the layer call of layer_decode_roofline: two
+    caches with the same contents alternate in a graph of 20 calls (more
+    than the last-level cache at these sizes), 10 warm-up replays, median
+    of 10.  Pack, prefill and tier calls are timed between HIP events."""
+    import torch
+    from bit_quantized_attention_two_amd import configs, minikv, synth
+    c = configs.get(config_id)
+    B, Hq, Hkv, D, n = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"]
+    Gk = c["Gk"]
+    dims = minikv.make_dims(B, Hq, Hkv, D, Gk, 16, c["residual_cap"])
+    ks, r = budgets(minikv, c)
+    m = int(ks[0]) + r
+    q, k, v = synth.gen_prefill_device(config_id, 0, "cuda", c)
+    dq, dk, dv = synth.gen_decode_device(config_id, 64, 1, "cuda", c)
+    ev = lambda: (torch.cuda.Event(enable_timing=True),
+                  torch.cuda.Event(enable_timing=True))
+
+    def timed(fn):
+        a, b = ev()
+        a.record(stream)
+        out = fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return out, a.elapsed_time(b)
+
+    def decode_time(caches):
+        o = torch.empty((B, Hq, D), dtype=torch.float16, device="cuda")
+        ws = torch.zeros(minikv.decode_mixed_ws_bytes(dims, caches[0]),
+                         dtype=torch.uint8, device="cuda")
+        R = 20
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            minikv.decode_mixed(dims, caches[0], dq[0, 0], o=o, ws=ws)
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=side):
+                for i in range(R):
+                    minikv.decode_mixed(dims, caches[i % 2], dq[0, 0], o=o, ws=ws)
+        stream.wait_stream(side)
+        for _ in range(10):
+            gr.replay()
+        ts = []
+        for _ in range(10):
+            a, b = ev()
+            a.record(stream)
+            gr.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts)) * 1e3 / R
+
+    def fill_residual(cache):
+        for t in range(64 - cache.n_res):
+            minikv.append_mixed(dims, cache, dk[t, 0], dv[t, 0])
+
+    recs = {}
+    # ---- MiKV
+    _, _, sel = minikv.prefill_select(dims, q, k, v, int(ks[0]), r)
+    segs = [(4, 4, (m // Gk) * Gk + 256), (2, 2, ((n - m) // Gk) * Gk + Gk)]
+    caches, pack_ms = [], []
+    for _ in range(2):
+        mc = minikv.MixedCache(dims, segs, flush_seg=0)
+        _, ms = timed(lambda: minikv.pack_mikv(dims, k, v, sel, mc))
+        pack_ms.append(ms)
+        fill_residual(mc)
+        caches.append(mc)
+    units = B * Hkv
+    seg_tok = [(4, 4, caches[0].n_packed(0) * units), (2, 2, caches[0].n_packed(1) * units)]
+    alg = mixed_decode_bytes(c, seg_tok, caches[0].n_res)
+    us = decode_time(caches)
+    recs["mikv"] = {
+        "workload": "%s layer 0: %d kv heads x (%d INT4 + %d INT2 packed + %d fp16 "
+                    "residual tokens)" % (c["name"], units, caches[0].n_packed(0),
+                                          caches[0].n_packed(1), caches[0].n_res),
+        "decode": {"bound": "hbm", "achieved": round(alg / (us * 1e-6) / 1e9, 2),
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "avg_launch_us": round(us, 3), "algorithmic_bytes_per_launch": alg},
+        "pack_mikv_ms": round(min(pack_ms), 3),
+        "average_code_bits": round(sum(kb * t for kb, _, t in seg_tok) /
+                                   max(1, sum(t for _, _, t in seg_tok)), 3),
+    }
+    del caches, sel
+    torch.cuda.empty_cache()
+    # ---- DiffKV
+    score = torch.empty((B, Hkv, n), dtype=torch.float32, device="cuda")
+    o_pre = torch.empty_like(q)
+    ws_pre = torch.empty(minikv.prefill_ws_bytes(dims, n), dtype=torch.uint8,
+                         device="cuda")
+    minikv.prefill_diffkv(dims, q, k, v, o=o_pre, score=score, ws=ws_pre)
+    _, pre_ms = timed(lambda: minikv.prefill_diffkv(dims, q, k, v, o=o_pre, score=score,
+                                                    ws=ws_pre))
+    tiers, tier_ms = timed(lambda: minikv.tier_diffkv(dims, score, *alphas))
+    idx_hi, idx_lo, n_hi, n_lo = tiers
+    bound = n // Gk * Gk
+    nh, nl = n_hi.cpu().numpy(), n_lo.cpu().numpy()
+    dsegs = [(8, 4, bound), (4, 2, bound), (8, 4, 256)]
+    caches, pack_ms = [], []
+    for _ in range(2):
+        mc = minikv.MixedCache(dims, dsegs, flush_seg=2)
+        _, ms = timed(lambda: minikv.pack_diffkv(dims, k, v, idx_hi, idx_lo, n_hi, n_lo, mc))
+        pack_ms.append(ms)
+        # the host reads the per-head counts back once and narrows the grid
+        mc.set_bound(0, int(nh.max()))
+        mc.set_bound(1, int(nl.max()))
+        fill_residual(mc)
+        caches.append(mc)
+    seg_tok = [(8, 4, int(nh.sum())), (4, 2, int(nl.sum()))]
+    alg = mixed_decode_bytes(c, seg_tok, caches[0].n_res)
+    us = decode_time(caches)
+    pre_fl = prefill_flops(c)
+    recs["diffkv"] = {
+        "workload": "%s layer 0: %d kv heads, alpha_hi %g, alpha_lo %g" % (
+            c["name"], units, alphas[0], alphas[1]),
+        "tier_tokens_per_kv_head": {"k8v4": nh.tolist(), "k4v2": nl.tolist(),
+                                    "pruned": (n - nh - nl).tolist()},
+        "prefill": {"bound": "mfma", "achieved": round(pre_fl / (pre_ms * 1e-3) / 1e12, 2),
+                    "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(pre_fl / (pre_ms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
+                    "call_ms": round(pre_ms, 3), "algorithmic_flops_per_launch": pre_fl},
+        "tier_ms": round(tier_ms, 3),
+        "pack_diffkv_ms": round(min(pack_ms), 3),
+        "decode": {"bound": "hbm", "achieved": round(alg / (us * 1e-6) / 1e9, 2),
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "avg_launch_us": round(us, 3), "algorithmic_bytes_per_launch": alg},
+    }
+    return recs
+
+
+def fused_tail_record(stream, config_id, reps=5):
+    """Layer 0 of a workload: minikv_prefill_select followed by minikv_pack,
+    against minikv_prefill_select_pack with the selection inside the second
+    prefill pass (fused) and after it; each a graph of one layer's calls
+    timed between HIP events, alternated `reps` times; medians."""
+    import torch
+    from bit_quantized_attention_two_amd import configs, minikv, synth
+    c = configs.get(config_id)
+    B, Hq, Hkv, D, n = c["B"], c["Hq"], c["Hkv"], c["D"], c["n"]
+    ks, r = budgets(minikv, c)
+    n_hh, m = int(ks[0]), int(ks[0]) + r
+    dims = minikv.make_dims(B, Hq, Hkv, D, c["Gk"], c["Gv"], c["residual_cap"])
+    q, k, v = synth.gen_prefill_device(config_id, 0, "cuda", c)
+    o = torch.empty_like(q)
+    col = torch.empty((B, Hkv, n), dtype=torch.float32, device="cuda")
+    sel = torch.empty((B, Hkv, m), dtype=torch.int32, device="cuda")
+    cache = minikv.LayerCache(dims, (m // c["Gk"]) * c["Gk"] + c["Gk"])
+    ws1 = torch.empty(minikv.prefill_ws_bytes(dims, n), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(minikv.prefill_tail_ws_bytes(dims, n), dtype=torch.uint8,
+                      device="cuda")
+
+    def separate():
+        minikv.prefill_select(dims, q, k, v, n_hh, r, o=o, col=col, sel=sel, ws=ws1)
+        minikv.pack(dims, k, v, sel, cache)
+
+    def fused():
+        minikv.prefill_select_pack(dims, q, k, v, n_hh, r, cache, fuse_select=True, o=o,
+                                   col=col, sel=sel, ws=ws2)
+
+    def one_call():
+        minikv.prefill_select_pack(dims, q, k, v, n_hh, r, cache, fuse_select=False, o=o,
+                                   col=col, sel=sel, ws=ws2)
+
+    graphs = []
+    side = torch.cuda.Stream()
+    for fn in (separate, fused, one_call):
+        fn()
+        side.wait_stream(stream)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=side):
+            fn()
+        stream.wait_stream(side)
+        graphs.append(gr)
+    ts = [[], [], []]
+    for _ in range(reps):
+        for i, gr in enumerate(graphs):
+            a, b = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            a.record(stream)
+            gr.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts[i].append(a.elapsed_time(b) * 1e3)
+    sep, fus, one = (float(np.median(t)) for t in ts)
+    return {"workload": "%s layer 0 (%d units, %d selected of %d)" % (
+                c["name"], B * Hkv, m, n),
+            "separate_calls_us": round(sep, 2),
+            "one_call_selection_kernel_us": round(one, 2),
+            "one_call_fused_selection_us": round(fus, 2),
+            "fused_saved_pct": round(100 * (sep - fus) / sep, 2)}
+
+
 def persistence_audit(st, layer=0, every=32):
     """The persistence test the MiniKV verdict record's falsifier asks for,
     on this workload's synthetic inputs: would the heavy hitters chosen at
@@ -680,6 +911,18 @@ def main():
         subs[sub["workload"]] = sub
     if subs:
         result["sub_records"] = subs
+    if not args.no_mixed:
+        mixed = {}
+        for cid in [int(x) for x in args.mixed_configs.split(",") if x.strip()]:
+            from bit_quantized_attention_two_amd import configs
+            mixed[configs.get(cid)["name"]] = mixed_records(stream, cid)
+            torch.cuda.empty_cache()
+            log("mixed-precision records of workload %d done" % cid)
+        result["mixed_precision"] = mixed
+    if not args.no_fused_tail:
+        result["fused_prefill_tail"] = [fused_tail_record(stream, cid)
+                                        for cid in (2, 4, 5)]
+        log("fused prefill tail records done")
     print(json.dumps(result), flush=True)
 
 

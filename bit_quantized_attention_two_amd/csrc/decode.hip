@@ -73,8 +73,10 @@ struct DecArgs {
     float qscale;
     const uint16_t *k_new, *v_new;   // nullable: fused append of one token
     int new_slot;                    // residual slot of the new token
-    float *part_ml;                  // [units][nsplit][G][2]
-    float *part_o;                   // [units][nsplit][G][D]
+    int split_off, nsplit_total;     // this launch's splits start at
+                                     //   split_off of nsplit_total per unit
+    float *part_ml;                  // [units][nsplit_total][G][2]
+    float *part_o;                   // [units][nsplit_total][G][D]
     float *lg;                       // nullable: logits out, log2 units,
     int lg_stride;                   //   [units][G][lg_stride], cache order
 };
@@ -115,6 +117,18 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ half8_t code_operand(uint32_t x) {
     const u32x4 v = {x & 0x00030003u, x & 0x000c000cu, x & 0x00300030u,
                      x & 0x00c000c0u};
+    return __builtin_bit_cast(half8_t, v);
+}
+
+// The same for 4-bit codes stored as two 2-bit planes (plane 1 = bits 2..3):
+// dword i holds (c0 + 4 c1) * 4^i * 2^-24 per half, at most 15 * 64 * 2^-24,
+// still an exact subnormal.  x0, x1: the two planes' words, shifted alike.
+__device__ __forceinline__ half8_t code_operand2(uint32_t x0, uint32_t x1) {
+    const uint32_t y = x1 << 2;
+    const u32x4 v = {(x0 & 0x00030003u) | (y & 0x000c000cu),
+                     (x0 & 0x000c000cu) | (y & 0x00300030u),
+                     (x0 & 0x00300030u) | (y & 0x00c000c0u),
+                     (x0 & 0x00c000c0u) | (y & 0x03000300u)};
     return __builtin_bit_cast(half8_t, v);
 }
 
@@ -171,15 +185,22 @@ struct alignas(16) WaveLds {
 // together with the key loads, so the wave waits for memory once instead
 // of once per phase; this is the form for small calls, whose time is the
 // latency of that chain rather than bandwidth.
-template <int D, int G, bool FULLV, bool ONE, bool MASS>
+//
+// KP, VP: 2-bit planes of the key and value codes (1: INT2; 2: 4-bit codes,
+// combined into one code operand; KP 4: 8-bit keys as a low and a high
+// 4-bit operand with their own accumulators, logit = low + 16 high).
+template <int D, int G, bool FULLV, bool ONE, bool MASS, int KP = 1, int VP = 1>
 __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                                             int nt, WaveLds<D, G> &L,
                                             float *m_out, float *l_out) {
+    static_assert(!ONE || (KP == 1 && VP == 1), "single-batch form is INT2 only");
     constexpr int KB = D / 32;                    // key k-blocks
     constexpr int KW = D / 16;                    // key words per token
     constexpr int NG16 = D / 16;                  // 16-channel value groups
     constexpr int NG = 16 / G;                    // key groups per B operand
-    constexpr int BT = G == 8 ? 32 : 64;          // tokens per key batch (within one key operand: 256 / G >= BT)
+    // tokens per key batch (within one key operand: 256 / G >= BT); planes
+    // multiply the key words held per batch, so those batches are halved
+    constexpr int BT = (G == 8 || KP > 1) ? 32 : 64;
     constexpr int TPB = BT / 16;                  // key tiles per batch
     constexpr int NPASS = (G * NG16 + 15) / 16;   // value passes
     constexpr int GPP = NG16 / NPASS;             // value groups per pass
@@ -193,6 +214,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     const uint16_t *qu = a.q + (size_t)unit * G * D;
     const uint32_t *kq = reinterpret_cast<const uint32_t *>(c.kq) +
                          (size_t)unit * c.kq_unit();
+    const size_t kpl = c.kplane(), vpl = c.vplane();
     const uint16_t *ks = c.ks + (size_t)unit * c.km_unit();
     const uint16_t *kz = c.kz + (size_t)unit * c.km_unit();
     const uint32_t *vq = reinterpret_cast<const uint32_t *>(c.vq) +
@@ -264,20 +286,29 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                     kz + (size_t)gz * D + 16 * w + 4 * (qd & 1) + 8 * hf);
         }
     };
-    uint32_t kw[TPB][KB];                         // key words of a batch
+    uint32_t kw[KP][TPB][KB];                     // key words of a batch
     auto load_kwords = [&](int tok) {
 #pragma unroll
         for (int j = 0; j < TPB; ++j) {
             const int t = min(tok + 16 * j + r, nt - 1);
-            const uint32_t *wp = kq + (uint32_t)((t0 + t) * KW + (qd >> 1) * KB);
-            if constexpr (KB == 4) {
-                const uint4 x = *reinterpret_cast<const uint4 *>(wp);
-                kw[j][0] = x.x; kw[j][1] = x.y; kw[j][2] = x.z; kw[j][3] = x.w;
-            } else {
-                const uint2 x = *reinterpret_cast<const uint2 *>(wp);
-                kw[j][0] = x.x; kw[j][1] = x.y;
+#pragma unroll
+            for (int pl = 0; pl < KP; ++pl) {
+                const uint32_t *wp = kq + pl * kpl + (uint32_t)((t0 + t) * KW + (qd >> 1) * KB);
+                if constexpr (KB == 4) {
+                    const uint4 x = *reinterpret_cast<const uint4 *>(wp);
+                    kw[pl][j][0] = x.x; kw[pl][j][1] = x.y; kw[pl][j][2] = x.z; kw[pl][j][3] = x.w;
+                } else {
+                    const uint2 x = *reinterpret_cast<const uint2 *>(wp);
+                    kw[pl][j][0] = x.x; kw[pl][j][1] = x.y;
+                }
             }
         }
+    };
+    // the key code operand of tile j, k-block kb, from planes pl, pl + 1
+    auto key_operand = [&](int j, int kb, int pl) -> half8_t {
+        const int sh = 8 * (qd & 1);
+        if constexpr (KP == 1) return code_operand(kw[0][j][kb] >> sh);
+        else return code_operand2(kw[pl][j][kb] >> sh, kw[pl + 1][j][kb] >> sh);
     };
 
     // key weights (B operand) from the scales in ksr
@@ -356,22 +387,27 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     // value words of pass P, 32-token step st: channels P CP + r MBP + mb
     // of the 16-token block that lane quarter qd >> 1 multiplies
     const int last_blk = (t0 + nt) / 16 - 1;
+    // (vw holds VP planes of MBP words: vw[pl * MBP + mb])
     auto load_vw = [&](int P, int st, uint32_t *vw) {
         const int blk = min((t0 + st) / 16 + (qd >> 1), last_blk);
-        const uint32_t *wp = vq + (uint32_t)(blk * D + P * CP + r * MBP);
-        if constexpr (MBP == 8) {
-            const uint4 x0 = *reinterpret_cast<const uint4 *>(wp);
-            const uint4 x1 = *reinterpret_cast<const uint4 *>(wp + 4);
-            vw[0] = x0.x; vw[1] = x0.y; vw[2] = x0.z; vw[3] = x0.w;
-            vw[4] = x1.x; vw[5] = x1.y; vw[6] = x1.z; vw[7] = x1.w;
-        } else if constexpr (MBP == 4) {
-            const uint4 x0 = *reinterpret_cast<const uint4 *>(wp);
-            vw[0] = x0.x; vw[1] = x0.y; vw[2] = x0.z; vw[3] = x0.w;
-        } else if constexpr (MBP == 2) {
-            const uint2 x0 = *reinterpret_cast<const uint2 *>(wp);
-            vw[0] = x0.x; vw[1] = x0.y;
-        } else {
-            vw[0] = wp[0];
+#pragma unroll
+        for (int pl = 0; pl < VP; ++pl) {
+            const uint32_t *wp = vq + pl * vpl + (uint32_t)(blk * D + P * CP + r * MBP);
+            uint32_t *w = vw + pl * MBP;
+            if constexpr (MBP == 8) {
+                const uint4 x0 = *reinterpret_cast<const uint4 *>(wp);
+                const uint4 x1 = *reinterpret_cast<const uint4 *>(wp + 4);
+                w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
+                w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
+            } else if constexpr (MBP == 4) {
+                const uint4 x0 = *reinterpret_cast<const uint4 *>(wp);
+                w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
+            } else if constexpr (MBP == 2) {
+                const uint2 x0 = *reinterpret_cast<const uint2 *>(wp);
+                w[0] = x0.x; w[1] = x0.y;
+            } else {
+                w[0] = wp[0];
+            }
         }
     };
 
@@ -382,7 +418,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     load_kwords(0);
     __builtin_amdgcn_sched_barrier(0);
     constexpr int NVE = ONE ? 2 : 1;              // value steps held early
-    uint32_t vwe[NPASS][NVE][MBP];
+    uint32_t vwe[NPASS][NVE][MBP * VP];
     if constexpr (ONE) {
         static_assert(BT == 64, "one key batch must cover the wave's tokens");
         load_vmeta(0);
@@ -429,9 +465,20 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const half8_t av = code_operand(kw[j][kb] >> (8 * (qd & 1)));
+                const half8_t av = key_operand(j, kb, 0);
                 acc = mfma16(av, bhi[kb], acc);
                 acc = mfma16(av, blo[kb], acc);
+            }
+            if constexpr (KP == 4) {              // the high 4 bits of 8-bit codes
+                float4_t acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const half8_t av = key_operand(j, kb, 2);
+                    acc2 = mfma16(av, bhi[kb], acc2);
+                    acc2 = mfma16(av, blo[kb], acc2);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(acc2[i], 16.f, acc[i]);
             }
             if (per_lane) {
                 if (tok + 16 * j < nt && gcol == tl / Gk - gb) keep = acc;
@@ -541,7 +588,13 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             const int vg = P * GPP + r % GPP;
             half8_t av[MBP];
 #pragma unroll
-            for (int mb = 0; mb < MBP; ++mb) av[mb] = code_operand(code(P, mb) >> (8 * (qd & 1)));
+            for (int mb = 0; mb < MBP; ++mb) {
+                if constexpr (VP == 1)
+                    av[mb] = code_operand(code(P, mb) >> (8 * (qd & 1)));
+                else
+                    av[mb] = code_operand2(code(P, mb) >> (8 * (qd & 1)),
+                                           code(P, MBP + mb) >> (8 * (qd & 1)));
+            }
             after(P);
             const half_t *sp = &L.sv[vg * kSvStride + st + tb];
             const half_t *zp = &L.zv[vg * kSvStride + st + tb];
@@ -578,7 +631,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         }
     } else {
         // value words two steps ahead: buffer A holds even steps, B odd
-        uint32_t vwA[NPASS][MBP], vwB[NPASS][MBP];
+        uint32_t vwA[NPASS][MBP * VP], vwB[NPASS][MBP * VP];
 #pragma unroll
         for (int P = 0; P < NPASS; ++P) load_vw(P, 0, vwA[P]);
 #pragma unroll
@@ -768,8 +821,10 @@ __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0
 // FULLV: value channel groups of 16 (D/16 scales per token).
 // MASS: also store every token's logit for the persistence audit.
 // W: waves per block, each with a chunk / W share of the split's tokens.
-template <int D, int G, bool FULLV, bool ONE, bool MASS, int W = kWaves>
-__global__ __launch_bounds__(W * 64, (G == 2 || G == 8) ? 2 : 3) void decode_kernel(DecArgs a) {
+// KP, VP: 2-bit planes of the key / value codes (packed_wave).
+template <int D, int G, bool FULLV, bool ONE, bool MASS, int W = kWaves, int KP = 1,
+          int VP = 1>
+__global__ __launch_bounds__(W * 64, (G == 2 || G == 8 || KP == 4) ? 2 : 3) void decode_kernel(DecArgs a) {
     // x = unit, y = split: with the round-robin dispatch of workgroups over
     // the 8 XCDs, every split of a unit (and its merge below) runs on the
     // XCD unit mod 8 when the unit count is a multiple of 8.
@@ -795,10 +850,14 @@ __global__ __launch_bounds__(W * 64, (G == 2 || G == 8) ? 2 : 3) void decode_ker
     // of its own.
     const bool res_role = split == a.res_split && wave >= a.res_wave0;
     if (!res_role && split < a.n_chunks) {
+        // a segment with per-unit counts: the grid covers the largest, and
+        // this unit's waves past its own count have no tokens
+        const int n_packed = c.n_unit ? min(c.n_unit[unit], a.n_packed) : a.n_packed;
         const int wchunk = a.chunk / W;
         const int t0 = split * a.chunk + wave * wchunk;
-        const int nt = max(0, min(wchunk, a.n_packed - t0));
-        if (nt > 0) packed_wave<D, G, FULLV, ONE, MASS>(a, unit, t0, nt, lds[wave], m_w, l_w);
+        const int nt = max(0, min(wchunk, n_packed - t0));
+        if (nt > 0)
+            packed_wave<D, G, FULLV, ONE, MASS, KP, VP>(a, unit, t0, nt, lds[wave], m_w, l_w);
     } else if (res_role) {
         const int nrw = W - a.res_wave0, rw = wave - a.res_wave0;
         const int per = (a.n_res + nrw - 1) / nrw;
@@ -836,7 +895,7 @@ __global__ __launch_bounds__(W * 64, (G == 2 || G == 8) ? 2 : 3) void decode_ker
         mrg[tid][1] = L;
     }
     __syncthreads();
-    const size_t sbase = (size_t)unit * a.nsplit + split;
+    const size_t sbase = (size_t)unit * a.nsplit_total + a.split_off + split;
     for (int i = tid; i < G * D; i += (W * 64)) {
         const int h = i / D;
         const float M = mrg[h][0];
@@ -982,25 +1041,34 @@ int pick_chunk(int units, int n_packed, int Gk, int g, bool mass) {
     return ch4;
 }
 
+// One launch of the decode kernel for the split plan in `a` (grid: units x
+// a.nsplit splits, written at a.split_off of a.nsplit_total).
 template <int D, int G>
-hipError_t launch_decode_dg(const DecArgs &a, int units, float *ml_out,
-                            const MassOut *mo, hipStream_t stream) {
+void decode_kernel_launch(const DecArgs &a, int units, bool mass, hipStream_t stream) {
+    const dim3 grid(units, a.nsplit);
+    if (a.c.kp != 1 || a.c.vp != 1) {
+        // a mixed-precision segment: 16-channel value groups, 4-wave blocks
+        if (a.c.kp == 2 && a.c.vp == 2)
+            decode_kernel<D, G, true, false, false, kWaves, 2, 2><<<grid, kThreads, 0, stream>>>(a);
+        else if (a.c.kp == 4 && a.c.vp == 2)
+            decode_kernel<D, G, true, false, false, kWaves, 4, 2><<<grid, kThreads, 0, stream>>>(a);
+        else
+            decode_kernel<D, G, true, false, false, kWaves, 2, 1><<<grid, kThreads, 0, stream>>>(a);
+        return;
+    }
     // one key batch per wave (64-token wave shares): the early-load form,
     // for g <= 2 (at g = 4 its registers would spill)
     const bool one = G <= 2 && a.chunk == kMinWaveChunk * kWaves;
-    const dim3 grid(units, a.nsplit);
-    bool big = false;
     if constexpr (G == 4) {
         if (a.waves == kBigWaves) {
-            big = true;
             if (a.c.Gv == 16)
                 decode_kernel<D, G, true, false, false, kBigWaves><<<grid, kBigWaves * 64, 0, stream>>>(a);
             else
                 decode_kernel<D, G, false, false, false, kBigWaves><<<grid, kBigWaves * 64, 0, stream>>>(a);
+            return;
         }
     }
-    if (big) {
-    } else if (mo) {
+    if (mass) {
         if (a.c.Gv == 16) {
             if (one) decode_kernel<D, G, true, G <= 2, true><<<grid, kThreads, 0, stream>>>(a);
             else decode_kernel<D, G, true, false, true><<<grid, kThreads, 0, stream>>>(a);
@@ -1015,14 +1083,32 @@ hipError_t launch_decode_dg(const DecArgs &a, int units, float *ml_out,
         if (one) decode_kernel<D, G, false, G <= 2, false><<<grid, kThreads, 0, stream>>>(a);
         else decode_kernel<D, G, false, false, false><<<grid, kThreads, 0, stream>>>(a);
     }
+}
+
+template <int D, int G>
+hipError_t launch_decode_dg(const DecArgs &a, int units, float *ml_out,
+                            const MassOut *mo, hipStream_t stream) {
+    decode_kernel_launch<D, G>(a, units, mo != nullptr, stream);
     decode_combine_kernel<D, G><<<dim3(units, G), kThreads, 0, stream>>>(
-        a.part_ml, a.part_o, a.nsplit, a.o, ml_out);
+        a.part_ml, a.part_o, a.nsplit_total, a.o, ml_out);
     if (mo) {
         const int n_tok = a.n_packed + a.n_res;
         decode_mass_kernel<G><<<dim3(units, (n_tok + kThreads - 1) / kThreads), kThreads, 0,
                                 stream>>>(a.lg, a.lg_stride, ml_out, n_tok, mo->mass,
                                           mo->stride);
     }
+    return hipGetLastError();
+}
+
+// Several packed segments (mixed precision) plus the residual: one decode
+// launch per segment into consecutive split ranges, then one combine.
+template <int D, int G>
+hipError_t launch_decode_segs_dg(const DecArgs *as, int n_seg, int units,
+                                 hipStream_t stream) {
+    for (int s = 0; s < n_seg; ++s)
+        if (as[s].nsplit > 0) decode_kernel_launch<D, G>(as[s], units, false, stream);
+    decode_combine_kernel<D, G><<<dim3(units, G), kThreads, 0, stream>>>(
+        as[0].part_ml, as[0].part_o, as[0].nsplit_total, as[0].o, nullptr);
     return hipGetLastError();
 }
 
@@ -1034,6 +1120,18 @@ hipError_t launch_decode_d(const DecArgs &a, int units, int g, float *ml_out,
     case 2: return launch_decode_dg<D, 2>(a, units, ml_out, mo, stream);
     case 4: return launch_decode_dg<D, 4>(a, units, ml_out, mo, stream);
     case 8: return launch_decode_dg<D, 8>(a, units, ml_out, mo, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int D>
+hipError_t launch_decode_segs_d(const DecArgs *as, int n_seg, int units, int g,
+                                hipStream_t stream) {
+    switch (g) {
+    case 1: return launch_decode_segs_dg<D, 1>(as, n_seg, units, stream);
+    case 2: return launch_decode_segs_dg<D, 2>(as, n_seg, units, stream);
+    case 4: return launch_decode_segs_dg<D, 4>(as, n_seg, units, stream);
+    case 8: return launch_decode_segs_dg<D, 8>(as, n_seg, units, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1104,9 +1202,11 @@ struct Plan {
     int chunk, waves, n_chunks, nsplit, res_split, res_wave0;
 };
 
-static Plan make_plan(int units, int g, int n_packed, int n_res, int Gk, bool mass) {
+// no_big: keep the 4-wave form (the mass audit and the 4- and 8-bit
+// segments have no 12-wave form).
+static Plan make_plan(int units, int g, int n_packed, int n_res, int Gk, bool no_big) {
     Plan p;
-    p.chunk = pick_chunk(units, n_packed, Gk, g, mass);
+    p.chunk = pick_chunk(units, n_packed, Gk, g, no_big);
     p.waves = p.chunk % kBigWaves == 0 ? kBigWaves : kWaves;   // W = 4 chunks are 2^k
     p.n_chunks = (n_packed + p.chunk - 1) / p.chunk;
     p.nsplit = p.n_chunks;
@@ -1156,6 +1256,8 @@ hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
     a.nsplit = p.nsplit;
     a.res_split = p.res_split;
     a.res_wave0 = p.res_wave0;
+    a.split_off = 0;
+    a.nsplit_total = p.nsplit;
     a.qscale = kLog2e / sqrtf((float)c.D);
     a.k_new = k_new;
     a.v_new = v_new;
@@ -1180,6 +1282,79 @@ hipError_t launch_decode(const uint16_t *q, uint16_t *o, int units, int g,
     }
     return c.D == 128 ? launch_decode_d<128>(a, units, g, ml_out, mo, stream)
                       : launch_decode_d<64>(a, units, g, ml_out, mo, stream);
+}
+
+// Split plans of a mixed-precision decode: segment s covers n_bound[s]
+// packed tokens per unit (its largest per-unit count when it has per-unit
+// counts); the residual runs with the last segment.  Returns the total
+// number of splits, or -1 if a segment needs more than kMaxSplit.
+static int plan_segments(int units, int g, const CacheView *segs, const int *n_bound,
+                         int n_seg, int n_res, Plan *plans) {
+    int total = 0;
+    for (int s = 0; s < n_seg; ++s) {
+        const bool planes = segs[s].kp != 1 || segs[s].vp != 1;
+        plans[s] = make_plan(units, g, n_bound[s], s == n_seg - 1 ? n_res : 0, segs[s].Gk,
+                             planes);
+        if (plans[s].nsplit > kMaxSplit) return -1;
+        total += plans[s].nsplit;
+    }
+    return total;
+}
+
+size_t decode_segs_ws_bytes(int units, int g, int D, const int *caps, int n_seg) {
+    int total = 1;                                // the residual's own split
+    for (int s = 0; s < n_seg; ++s)
+        total += std::min((caps[s] + kMinWaveChunk * kWaves - 1) / (kMinWaveChunk * kWaves),
+                          kMaxSplit);
+    return part_bytes(units, g, D, total);
+}
+
+size_t decode_segs_plan_ws_bytes(int units, int g, int D, const CacheView *segs,
+                                 const int *n_bound, int n_seg, int n_res) {
+    Plan plans[kMaxSegments];
+    const int total = plan_segments(units, g, segs, n_bound, n_seg, n_res, plans);
+    return total < 0 ? 0 : part_bytes(units, g, D, total);
+}
+
+hipError_t launch_decode_segs(const uint16_t *q, uint16_t *o, int units, int g,
+                              const CacheView *segs, const int *n_bound, int n_seg,
+                              int n_res, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (n_seg < 1 || n_seg > kMaxSegments) return hipErrorInvalidValue;
+    Plan plans[kMaxSegments];
+    const int total = plan_segments(units, g, segs, n_bound, n_seg, n_res, plans);
+    const int D = segs[0].D;
+    // checked by the entry point before any HIP call
+    if (total < 0 || part_bytes(units, g, D, total) > ws_bytes) return hipErrorInvalidValue;
+    DecArgs as[kMaxSegments];
+    int off = 0;
+    for (int s = 0; s < n_seg; ++s) {
+        DecArgs &a = as[s];
+        const Plan &p = plans[s];
+        a.q = q;
+        a.o = o;
+        a.c = segs[s];
+        a.n_packed = n_bound[s];
+        a.n_res = s == n_seg - 1 ? n_res : 0;
+        a.chunk = p.chunk;
+        a.waves = p.waves;
+        a.n_chunks = p.n_chunks;
+        a.nsplit = p.nsplit;
+        a.res_split = p.res_split;
+        a.res_wave0 = p.res_wave0;
+        a.split_off = off;
+        a.nsplit_total = total;
+        a.qscale = kLog2e / sqrtf((float)D);
+        a.k_new = nullptr;
+        a.v_new = nullptr;
+        a.new_slot = -1;
+        a.part_ml = static_cast<float *>(ws);
+        a.part_o = a.part_ml + (size_t)units * total * g * 2;
+        a.lg = nullptr;
+        a.lg_stride = 0;
+        off += p.nsplit;
+    }
+    return D == 128 ? launch_decode_segs_d<128>(as, n_seg, units, g, stream)
+                    : launch_decode_segs_d<64>(as, n_seg, units, g, stream);
 }
 
 }  // namespace minikv

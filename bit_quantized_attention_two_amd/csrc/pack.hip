@@ -1,4 +1,5 @@
-// INT2 asymmetric packing of selected KV tokens (KIVI-style), gfx950.
+// INT2 (and 4-/8-bit) asymmetric packing of selected KV tokens (KIVI-style),
+// gfx950.
 //
 // Pith review of MiniKV, "Assumptions & free parameters": keys are quantised
 // per channel over groups of 16 tokens, values per token over groups of 16
@@ -13,6 +14,17 @@
 // of x is decided by exact comparisons of d = x - zero against (c + 1/2) *
 // scale (exact products), i.e. round-half-even of d / scale clamped to
 // [0, 3].  Contraction into FMAs is switched off for this file.
+//
+// Mixed-precision caches ("Don't Discard, but Keep It Small", the authors'
+// response on the implementation: tokens regrouped by precision, each group
+// stored contiguously at its own bit width; DiffKV's verdict record: keys at
+// 8 or 4 bits, values at 4 or 2) use the same codec with 2^b - 1 in place of
+// 3: the code is the round-half-even of the exact d / scale clamped to
+// [0, 2^b - 1].  With 15 or 255 thresholds, the code is first estimated from
+// the correctly rounded quotient d / scale (which is off by at most one) and
+// then settled by the same exact comparisons against (j + 1/2) * scale.  A
+// b-bit code is stored as b/2 planes of 2-bit codes, each plane in the INT2
+// word layout.
 #pragma clang fp contract(off)
 
 #include "common.h"
@@ -26,10 +38,11 @@ struct QParams {
     float sf, zf, t0, t1, t2;
 };
 
+template <int BITS>
 __device__ __forceinline__ QParams qparams(float mn, float mx) {
     QParams p;
     float range = __fsub_rn(mx, mn);
-    float s32 = __fdiv_rn(range, 3.0f);
+    float s32 = __fdiv_rn(range, (float)((1 << BITS) - 1));
     p.sh = f2h_bits(s32);
     p.zh = f2h_bits(__fadd_rn(mn, 0.0f));
     p.sf = h2f(p.sh);
@@ -40,11 +53,28 @@ __device__ __forceinline__ QParams qparams(float mn, float mx) {
     return p;
 }
 
+template <int BITS>
 __device__ __forceinline__ uint32_t code_of(float x, const QParams &p) {
     if (p.sf == 0.0f) return 0u;
     float d = __fsub_rn(x, p.zf);
-    return (uint32_t)(d > p.t0) + (uint32_t)(d >= p.t1) +
-           (uint32_t)(d > p.t2);
+    if constexpr (BITS == 2) {
+        return (uint32_t)(d > p.t0) + (uint32_t)(d >= p.t1) +
+               (uint32_t)(d > p.t2);
+    } else {
+        // code = #{j < top : d > T_j, or d == T_j with j odd}, T_j = (j + 1/2)
+        // scale exact; the set of such j is 0 .. code - 1, and the rounded
+        // quotient lands on code or a neighbour of it
+        constexpr int top = (1 << BITS) - 1;
+        auto above = [&](int j) {
+            const float t = __fmul_rn(__fadd_rn((float)j, 0.5f), p.sf);
+            return d > t || (d == t && (j & 1));
+        };
+        int c = (int)__builtin_rintf(__fdiv_rn(d, p.sf));
+        c = min(max(c, 0), top);
+        if (c > 0 && !above(c - 1)) --c;
+        if (c < top && above(c)) ++c;
+        return (uint32_t)c;
+    }
 }
 
 // OR of a value over the 16 lanes of a DPP row; every lane gets the result.
@@ -70,14 +100,16 @@ __device__ __forceinline__ void unpack8(uint4 x, float *f) {
 // read each 16-row chunk again for the codes; the second read hits the
 // cache).  A key word holds 16 channels of one token, so the two threads of
 // a 16-channel block combine their halves of each word.
-template <int D>
+template <int D, int BITS>
 __global__ __launch_bounds__(256) void pack_keys_kernel(
     PackSrc src, int n_groups, int dst_group_off, CacheView c) {
     constexpr int TPG = D / 8;                   // threads per group
     constexpr int GPB = 256 / TPG;               // groups per block
+    constexpr int KP = BITS / 2;                 // 2-bit planes
     const int unit = blockIdx.y;
     const int gi = blockIdx.x * GPB + threadIdx.x / TPG;
     const int oct = threadIdx.x % TPG;           // channels 8 oct .. 8 oct + 7
+    if (c.n_unit) n_groups = min(n_groups, c.n_unit[unit] / c.Gk);
     if (gi >= n_groups) return;                  // whole channel blocks leave
     const int Gk = c.Gk;
     const uint16_t *base = src.k + (size_t)unit * src.src_unit + oct * 8;
@@ -118,7 +150,7 @@ __global__ __launch_bounds__(256) void pack_keys_kernel(
     }
     QParams qp[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qp[j] = qparams(mn[j], mx[j]);
+    for (int j = 0; j < 8; ++j) qp[j] = qparams<BITS>(mn[j], mx[j]);
 
     const int g_out = dst_group_off + gi;
     int32_t *kq = c.kq + (size_t)unit * c.kq_unit() +
@@ -130,11 +162,20 @@ __global__ __launch_bounds__(256) void pack_keys_kernel(
         for (int i = 0; i < RB; ++i) {
             float x[8];
             unpack8(rr[i], x);
-            uint32_t half = 0;
+            uint32_t half[KP] = {};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) half |= code_of(x[j], qp[j]) << (sh + 2 * j);
-            const uint32_t word = half | (uint32_t)__shfl_xor((int)half, 1);
-            if ((oct & 1) == 0) kq[(size_t)(t0 + i) * (D / 16)] = (int32_t)word;
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t code = code_of<BITS>(x[j], qp[j]);
+#pragma unroll
+                for (int pl = 0; pl < KP; ++pl)
+                    half[pl] |= ((code >> (2 * pl)) & 3u) << (sh + 2 * j);
+            }
+#pragma unroll
+            for (int pl = 0; pl < KP; ++pl) {
+                const uint32_t word = half[pl] | (uint32_t)__shfl_xor((int)half[pl], 1);
+                if ((oct & 1) == 0)
+                    kq[pl * c.kplane() + (size_t)(t0 + i) * (D / 16)] = (int32_t)word;
+            }
         }
     }
     const size_t mo = (size_t)unit * c.km_unit() + (size_t)g_out * D + oct * 8;
@@ -158,13 +199,19 @@ __global__ __launch_bounds__(256) void pack_keys_kernel(
 // rows of K and V, unchanged, into residual slots 0..n_tail-1 (the ragged
 // tail of the selection stays fp16), 16 bytes each.  The boundary falls on
 // a multiple of 16 threads, so no DPP row mixes the two kinds.
-template <int D>
+template <int D, int BITS>
 __global__ __launch_bounds__(256) void pack_values_kernel(
-    PackSrc src, int n_tok, int n_tail, int dst_off, CacheView c) {
+    PackSrc src, int n_tok, int n_tail, int dst_off, CacheView c,
+    int tail_off) {
+    constexpr int VP = BITS / 2;                 // 2-bit planes
     const int unit = blockIdx.y;
     const int Gv = c.Gv;
     const int gpt = D / Gv;                      // groups per token
     const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (c.n_unit) {                              // this unit's own count
+        n_tok = min(n_tok, c.n_unit[unit]);
+        if (idx >= n_tok * gpt) return;          // (no tail with counts)
+    }
     if (idx >= n_tok * gpt) {
         constexpr int PER_ROW = D / 8;           // uint4 per row
         const int tidx = idx - n_tok * gpt;
@@ -176,7 +223,7 @@ __global__ __launch_bounds__(256) void pack_values_kernel(
                                            (uint32_t)(src.n_rows - 1))
                                 : p;
         const size_t s_off = (size_t)unit * src.src_unit + (size_t)row * D;
-        const size_t d_off = (size_t)unit * c.res_unit() + (size_t)slot * D;
+        const size_t d_off = (size_t)unit * c.res_unit() + (size_t)(tail_off + slot) * D;
         reinterpret_cast<uint4 *>(c.kres + d_off)[part] =
             reinterpret_cast<const uint4 *>(src.k + s_off)[part];
         reinterpret_cast<uint4 *>(c.vres + d_off)[part] =
@@ -209,23 +256,28 @@ __global__ __launch_bounds__(256) void pack_values_kernel(
             }
         }
     }
-    const QParams qp = qparams(mn, mx);
+    const QParams qp = qparams<BITS>(mn, mx);
 
     const int t_out = dst_off + p;
     int32_t *vq = c.vq + (size_t)unit * c.vq_unit() +
                   (size_t)(t_out >> 4) * D + G * Gv + e;
     for (int wi = 0; wi < Gv / 16; ++wi) {
-        uint32_t mine = 0;
+        uint32_t mine[VP] = {};
         for (int hh = 0; hh < 2; ++hh) {
             float x[8];
             unpack8(x4[wi * 2 + hh], x);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const uint32_t w = row16_or(code_of(x[j], qp) << (2 * e));
-                if (hh * 8 + j == e) mine = w;
+                const uint32_t code = code_of<BITS>(x[j], qp);
+#pragma unroll
+                for (int pl = 0; pl < VP; ++pl) {
+                    const uint32_t w = row16_or(((code >> (2 * pl)) & 3u) << (2 * e));
+                    if (hh * 8 + j == e) mine[pl] = w;
+                }
             }
         }
-        vq[wi * 16] = (int32_t)mine;
+#pragma unroll
+        for (int pl = 0; pl < VP; ++pl) vq[pl * c.vplane() + wi * 16] = (int32_t)mine[pl];
     }
     const size_t mo = (size_t)unit * c.vm_unit() + (size_t)t_out * gpt + G;
     c.vs[mo] = qp.sh;
@@ -247,28 +299,80 @@ __global__ __launch_bounds__(256) void append_copy_kernel(
         reinterpret_cast<const uint4 *>(v_new + (size_t)unit * c.D)[part];
 }
 
-}  // namespace
 
-hipError_t launch_pack(const PackSrc &src, int units, int n_tok, int n_tail,
-                       int dst_off, const CacheView &c, hipStream_t stream) {
+template <int D, int KB, int VB>
+void pack_launch_dbits(const PackSrc &src, int units, int n_tok, int n_tail,
+                       int dst_off, const CacheView &c, hipStream_t stream,
+                       int tail_off) {
     if (n_tok > 0) {
         const int n_groups = n_tok / c.Gk;
-        const int gpb = 256 / (c.D / 8);
+        const int gpb = 256 / (D / 8);
         dim3 gk((n_groups + gpb - 1) / gpb, units);
-        if (c.D == 128)
-            pack_keys_kernel<128><<<gk, 256, 0, stream>>>(src, n_groups, dst_off / c.Gk, c);
-        else
-            pack_keys_kernel<64><<<gk, 256, 0, stream>>>(src, n_groups, dst_off / c.Gk, c);
+        pack_keys_kernel<D, KB><<<gk, 256, 0, stream>>>(src, n_groups, dst_off / c.Gk, c);
     }
     if (n_tok + n_tail > 0) {
         // packed tokens' value threads (n_tok % 16 == 0), then the tail copy
-        const int vthreads = n_tok * (c.D / c.Gv) + n_tail * (c.D / 8);
+        const int vthreads = n_tok * (D / c.Gv) + n_tail * (D / 8);
         dim3 gv((vthreads + 255) / 256, units);
-        if (c.D == 128)
-            pack_values_kernel<128><<<gv, 256, 0, stream>>>(src, n_tok, n_tail, dst_off, c);
-        else
-            pack_values_kernel<64><<<gv, 256, 0, stream>>>(src, n_tok, n_tail, dst_off, c);
+        pack_values_kernel<D, VB><<<gv, 256, 0, stream>>>(src, n_tok, n_tail, dst_off, c,
+                                                          tail_off);
     }
+}
+
+template <int D>
+hipError_t pack_launch_d(const PackSrc &src, int units, int n_tok, int n_tail,
+                         int dst_off, const CacheView &c, hipStream_t stream,
+                         int tail_off) {
+    const int kb = 2 * c.kp, vb = 2 * c.vp;
+    if (kb == 2 && vb == 2)
+        pack_launch_dbits<D, 2, 2>(src, units, n_tok, n_tail, dst_off, c, stream, tail_off);
+    else if (kb == 4 && vb == 4)
+        pack_launch_dbits<D, 4, 4>(src, units, n_tok, n_tail, dst_off, c, stream, tail_off);
+    else if (kb == 8 && vb == 4)
+        pack_launch_dbits<D, 8, 4>(src, units, n_tok, n_tail, dst_off, c, stream, tail_off);
+    else if (kb == 4 && vb == 2)
+        pack_launch_dbits<D, 4, 2>(src, units, n_tok, n_tail, dst_off, c, stream, tail_off);
+    else
+        return hipErrorInvalidValue;            // validated by the entry points
+    return hipGetLastError();
+}
+
+// One thread per (unit, token j): j's position among the unselected tokens
+// is j minus the number of selected indices below it (a binary search of
+// the unit's ascending selection).
+__global__ __launch_bounds__(256) void complement_kernel(const int32_t *__restrict__ sel,
+                                                          int n, int m,
+                                                          int32_t *__restrict__ comp) {
+    const int unit = blockIdx.y;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= n) return;
+    const int32_t *s = sel + (size_t)unit * m;
+    int lo = 0, hi = m;                          // first index with s[i] >= j
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s[mid] < j) lo = mid + 1;
+        else hi = mid;
+    }
+    if (lo < m && s[lo] == j) return;
+    // a selection that is not strictly ascending in [0, n) leaves more
+    // unselected tokens than n - m; they are dropped, never written out of
+    // bounds
+    if (j - lo < n - m) comp[(size_t)unit * (n - m) + (j - lo)] = j;
+}
+
+}  // namespace
+
+hipError_t launch_pack(const PackSrc &src, int units, int n_tok, int n_tail,
+                       int dst_off, const CacheView &c, hipStream_t stream,
+                       int tail_off) {
+    return c.D == 128 ? pack_launch_d<128>(src, units, n_tok, n_tail, dst_off, c, stream, tail_off)
+                      : pack_launch_d<64>(src, units, n_tok, n_tail, dst_off, c, stream, tail_off);
+}
+
+hipError_t launch_complement(const int32_t *sel, int units, int n, int m,
+                             int32_t *comp, hipStream_t stream) {
+    if (n - m > 0)
+        complement_kernel<<<dim3((n + 255) / 256, units), 256, 0, stream>>>(sel, n, m, comp);
     return hipGetLastError();
 }
 

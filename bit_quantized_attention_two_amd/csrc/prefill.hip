@@ -16,6 +16,7 @@
 // MFMA: v_mfma_f32_32x32x16_f16 (fp16 inputs, fp32 accumulate).
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 // The compensated column sum below relies on each fp32 operation being
 // rounded separately.
@@ -23,6 +24,14 @@
 
 namespace minikv {
 namespace {
+
+// The fused prefill tail's selection: per-unit completion counters (zeroed
+// by pass 1) and the selection's arguments.
+struct TailArgs {
+    uint32_t *cnt;
+    int32_t *sel;
+    int n_hh, n_recent;
+};
 
 constexpr int kBM = 256;      // pass 1: queries per block (32 per wave)
 constexpr int kBN = 64;       // pass 1: keys per iteration
@@ -97,7 +106,11 @@ template <int D>
 __global__ __launch_bounds__(512, 1) void prefill_fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o,
-    float *__restrict__ lse, int Hq, int Hkv, int n, float sl2) {
+    float *__restrict__ lse, int Hq, int Hkv, int n, float sl2,
+    uint32_t *__restrict__ tail_cnt, int n_cnt) {
+    // the fused prefill tail's per-unit counters start each call at zero
+    if (tail_cnt && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i < n_cnt; i += blockDim.x) tail_cnt[i] = 0;
     constexpr int KS = D / 16;
     constexpr int DT = D / 32;
     constexpr int KPAD = D + 8;       // K row stride (halves): 4 dwords mod 64
@@ -378,16 +391,31 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_kernel(
 // past n get LSE = +inf, so their probabilities are exactly 0; sub-tiles
 // that reach the diagonal are masked (all of a sub-tile whose rows precede
 // the wave's keys is masked to 0).
-template <int D, int NC>
+//
+// MAXAGG (DiffKV's significance, verdict record for arXiv 2412.03131,
+// key_machinery): instead of summing over the kv head's g query heads, each
+// head's column sum is completed at the end of that head's tiles and the
+// maximum over heads is kept; the stored value is that maximum divided by
+// the number of rows that attend to the key, n - j (the average attention
+// the key receives).
+//
+// FUSESEL (the fused prefill tail): after storing its columns, every
+// workgroup adds one to its unit's counter (device scope, after a release
+// fence); the workgroup that completes the unit then runs the unit's
+// heavy-hitter + recent-window selection itself (topk.h, 256 threads, in the
+// LDS of the finished Q ring), so no separate selection launch follows and
+// the selection of a unit overlaps the other units' pass 2.
+template <int D, int NC, bool MAXAGG = false, bool FUSESEL = false>
 __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const float *__restrict__ lse, float *__restrict__ col, int Hq, int Hkv,
-    int n, float sl2) {
+    int n, float sl2, TailArgs tail) {
     constexpr int KS = D / 16;
     constexpr int QPAD = D + 8;
     constexpr int QLD = kBQ2 * D / 8 / 256;         // uint4 loads per thread
     __shared__ __attribute__((aligned(16))) uint16_t q_s[3][kBQ2 * QPAD];
     __shared__ __attribute__((aligned(16))) float lse_s[3][kBQ2];
+    static_assert(sizeof(SelLds<256>) <= sizeof(q_s), "selection LDS fits the Q ring");
 
     // x = unit, y = key block (block 0 has most rows, dispatched first);
     // with many units each XCD takes one unit's key blocks after another,
@@ -417,9 +445,9 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
     // Column sums: each 64-row tile is summed on its own, then added to a
     // compensated (Kahan) running sum, so tens of thousands of small
     // probabilities added to a large column total do not drift low.
-    float colacc[NC], colcomp[NC];
+    float colacc[NC], colcomp[NC], colmax[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) colacc[c] = colcomp[c] = 0.f;
+    for (int c = 0; c < NC; ++c) colacc[c] = colcomp[c] = colmax[c] = 0.f;
 
     // flattened (head, query tile) sequence
     const int qstart = kb * 128 * NC;
@@ -535,41 +563,87 @@ __global__ __launch_bounds__(256, 2) void prefill_col_kernel(
             colcomp[c] = (tt - colacc[c]) - y;
             colacc[c] = tt;
         }
+        if constexpr (MAXAGG) {
+            if ((t + 1) % tiles_per_head == 0) {   // a head's last tile (uniform)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    colmax[c] = fmaxf(colmax[c], colacc[c] + shfl_xor(colacc[c], 32));
+                    colacc[c] = colcomp[c] = 0.f;
+                }
+            }
+        }
         if (more) store_tile(t + 2);
         __syncthreads();
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const float tot = colacc[c] + shfl_xor(colacc[c], 32);
         const int key = k0w + 32 * c + l32;
-        if (hi == 0 && key < n) col[(size_t)unit * n + key] = tot;
+        if constexpr (MAXAGG) {
+            if (hi == 0 && key < n)
+                col[(size_t)unit * n + key] = __fdiv_rn(colmax[c], (float)(n - key));
+        } else {
+            const float tot = colacc[c] + shfl_xor(colacc[c], 32);
+            if (hi == 0 && key < n) col[(size_t)unit * n + key] = tot;
+        }
+    }
+    if constexpr (FUSESEL) {
+        __shared__ int s_last;
+        __syncthreads();                            // every wave's columns stored
+        if (tid == 0) {
+            __threadfence();                        // release them device-wide
+            s_last = atomicAdd(&tail.cnt[unit], 1u) == (uint32_t)gridDim.y - 1;
+        }
+        __syncthreads();
+        if (!s_last) return;                        // uniform
+        __threadfence();                            // acquire the other blocks' columns
+        SelLds<256> &L = *reinterpret_cast<SelLds<256> *>(&q_s[0][0]);
+        select_unit<256>(col + (size_t)unit * n, n, tail.n_hh, tail.n_recent,
+                         tail.sel + (size_t)unit * (tail.n_hh + tail.n_recent), L);
     }
 }
 
 }  // namespace
 
+template <int D, bool MAXAGG, bool FUSESEL = false>
+void launch_col(const dim3 &g2, bool wide, const uint16_t *q, const uint16_t *k,
+                const float *lse, float *col, int Hq, int Hkv, int n, float sl2,
+                hipStream_t stream, const TailArgs &tail = TailArgs{nullptr, nullptr, 0, 0}) {
+    if (wide)
+        prefill_col_kernel<D, 2, MAXAGG, FUSESEL><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq,
+                                                                          Hkv, n, sl2, tail);
+    else
+        prefill_col_kernel<D, 1, MAXAGG, FUSESEL><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq,
+                                                                          Hkv, n, sl2, tail);
+}
+
 hipError_t launch_prefill(const uint16_t *q, const uint16_t *k,
                           const uint16_t *v, uint16_t *o, float *lse,
                           float *col, int B, int Hq, int Hkv, int n, int D,
-                          hipStream_t stream) {
+                          hipStream_t stream, bool significance,
+                          const FusedSelect *fs) {
     const float sl2 = kLog2e / sqrtf((float)D);
     const dim3 g1(B * Hq, (n + kBM - 1) / kBM);
     // Pass 2 with 64 keys per wave unless that leaves too few workgroups
     // (short sequences) to balance the triangular work over the CUs.
     const bool wide = (long)B * Hkv * ((n + 255) / 256) >= 1024;
     const dim3 g2(B * Hkv, (n + (wide ? 255 : 127)) / (wide ? 256 : 128));
+    uint32_t *cnt = fs ? fs->counters : nullptr;
+    const TailArgs tail{cnt, fs ? fs->sel : nullptr, fs ? fs->n_hh : 0, fs ? fs->n_recent : 0};
+    const int units = B * Hkv;
     if (D == 128) {
-        prefill_fwd_kernel<128><<<g1, 512, 0, stream>>>(q, k, v, o, lse, Hq, Hkv, n, sl2);
-        if (wide)
-            prefill_col_kernel<128, 2><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
-        else
-            prefill_col_kernel<128, 1><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
+        prefill_fwd_kernel<128><<<g1, 512, 0, stream>>>(q, k, v, o, lse, Hq, Hkv, n, sl2, cnt,
+                                                        units);
+        if (significance) launch_col<128, true>(g2, wide, q, k, lse, col, Hq, Hkv, n, sl2, stream);
+        else if (fs) launch_col<128, false, true>(g2, wide, q, k, lse, col, Hq, Hkv, n, sl2,
+                                                  stream, tail);
+        else launch_col<128, false>(g2, wide, q, k, lse, col, Hq, Hkv, n, sl2, stream);
     } else {
-        prefill_fwd_kernel<64><<<g1, 512, 0, stream>>>(q, k, v, o, lse, Hq, Hkv, n, sl2);
-        if (wide)
-            prefill_col_kernel<64, 2><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
-        else
-            prefill_col_kernel<64, 1><<<g2, 256, 0, stream>>>(q, k, lse, col, Hq, Hkv, n, sl2);
+        prefill_fwd_kernel<64><<<g1, 512, 0, stream>>>(q, k, v, o, lse, Hq, Hkv, n, sl2, cnt,
+                                                       units);
+        if (significance) launch_col<64, true>(g2, wide, q, k, lse, col, Hq, Hkv, n, sl2, stream);
+        else if (fs) launch_col<64, false, true>(g2, wide, q, k, lse, col, Hq, Hkv, n, sl2,
+                                                 stream, tail);
+        else launch_col<64, false>(g2, wide, q, k, lse, col, Hq, Hkv, n, sl2, stream);
     }
     return hipGetLastError();
 }

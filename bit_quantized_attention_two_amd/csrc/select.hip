@@ -10,132 +10,84 @@
 // permutation of keys and values -- the MiKV rebuttal page on permutation
 // invariance).
 //
-// One workgroup per (batch, kv head).  The n_hh-th largest score is found by
-// a three-pass radix select (11 + 11 + 10 bits) over order-preserving 32-bit
-// keys built from the fp32 bits, histograms in LDS.  A final pass in index
-// order keeps every score above the threshold and the lowest-index scores
-// equal to it, compacting with wave ballots, so the output is ascending and
-// the whole result is exact and deterministic.
-#include "common.h"
+// One workgroup of 1024 threads per (batch, kv head); the selection itself
+// (a radix select and an ordered compaction) is in topk.h.
 #include "launch.h"
+#include "topk.h"
 
 namespace minikv {
 namespace {
 
 constexpr int kSelThreads = 1024;
-constexpr int kWaves = kSelThreads / 64;
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-    uint32_t b = __builtin_bit_cast(uint32_t, f);
-    if (b == 0x80000000u) b = 0u;                   // -0 ranks as +0
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// Exclusive prefix sum over the block in thread order; returns the thread's
-// exclusive prefix, and the block total through *total.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wsum,
-                                                    uint32_t *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t acc = 0;
-        for (int w = 0; w < kWaves; ++w) {
-            const uint32_t t = wsum[w];
-            wsum[w] = acc;
-            acc += t;
-        }
-        wsum[kWaves] = acc;
-    }
-    __syncthreads();
-    const uint32_t r = wsum[wave] + x - v;
-    *total = wsum[kWaves];
-    __syncthreads();
-    return r;
-}
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float *__restrict__ col, int n, int n_hh, int n_recent,
     int32_t *__restrict__ sel) {
+    __shared__ SelLds<kSelThreads> L;
+    const int unit = blockIdx.x;
+    select_unit<kSelThreads>(col + (size_t)unit * n, n, n_hh, n_recent,
+                             sel + (size_t)unit * (n_hh + n_recent), L);
+}
+
+// DiffKV tiers of one unit (one workgroup): the counts of significance
+// scores above the two thresholds, each rounded up to whole key groups;
+// the k-th largest key for both counts; then one pass in index order
+// writes the high tier (among the top c_hi) and the low tier (among the top
+// c_kept but not the top c_hi), both ascending.  The order is (score
+// descending, index ascending), so the top c_hi is part of the top c_kept.
+__global__ __launch_bounds__(kSelThreads) void tier_kernel(
+    const float *__restrict__ score, int n, float thr_hi, float thr_lo, int Gk,
+    int32_t *__restrict__ idx_hi, int32_t *__restrict__ idx_lo,
+    int32_t *__restrict__ n_hi, int32_t *__restrict__ n_lo) {
     const int unit = blockIdx.x;
     const int tid = threadIdx.x;
-    const float *c = col + (size_t)unit * n;
-    int32_t *out = sel + (size_t)unit * (n_hh + n_recent);
-    const int nc = n - n_recent;
-
-    for (int t = tid; t < n_recent; t += kSelThreads) out[n_hh + t] = nc + t;
-    if (n_hh == 0) return;
-    if (n_hh == nc) {
-        for (int t = tid; t < nc; t += kSelThreads) out[t] = t;
-        return;
+    const float *c = score + (size_t)unit * n;
+    __shared__ SelLds<kSelThreads> L;
+    __shared__ uint32_t s_cnt[2];
+    if (tid == 0) s_cnt[0] = s_cnt[1] = 0;
+    __syncthreads();
+    uint32_t a = 0, b = 0;
+    for (int j = tid; j < n; j += kSelThreads) {
+        a += c[j] > thr_hi ? 1u : 0u;
+        b += c[j] > thr_lo ? 1u : 0u;
     }
-
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t wsum[kWaves + 1];
-    __shared__ uint32_t s_bin, s_above;
-
-    uint32_t prefix = 0, pmask = 0;
-    uint32_t remaining = (uint32_t)n_hh;
-    const int shifts[3] = {21, 10, 0};
-    const int widths[3] = {11, 11, 10};
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = shifts[pass];
-        const int nb = 1 << widths[pass];
-        for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
-        __syncthreads();
-        for (int j = tid; j < nc; j += kSelThreads) {
-            const uint32_t u = order_key(c[j]);
-            if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
-        }
-        __syncthreads();
-        // thread t owns bins nb-1-bpt*t ... nb-bpt*(t+1), highest first
-        const int bpt = nb / kSelThreads;
-        const int top = nb - 1 - bpt * tid;
-        uint32_t mine = 0;
-        for (int i = 0; i < bpt; ++i) mine += hist[top - i];
-        uint32_t total;
-        uint32_t above = block_excl_scan(mine, wsum, &total);
-        if (above < remaining && remaining <= above + mine) {
-            for (int i = 0; i < bpt; ++i) {
-                const uint32_t h = hist[top - i];
-                if (remaining <= above + h) {
-                    s_bin = (uint32_t)(top - i);
-                    s_above = above;
-                    break;
-                }
-                above += h;
-            }
-        }
-        __syncthreads();
-        prefix |= s_bin << shift;
-        pmask |= (uint32_t)(nb - 1) << shift;
-        remaining -= s_above;
-        __syncthreads();
-    }
-    // prefix is the n_hh-th largest key; `remaining` equal keys are taken,
-    // lowest indices first.
-    const uint32_t T = prefix;
-    const uint32_t need_eq = remaining;
-    uint32_t base = 0, eq_seen = 0;
-    for (int t0 = 0; t0 < nc; t0 += kSelThreads) {
+    atomicAdd(&s_cnt[0], a);
+    atomicAdd(&s_cnt[1], b);
+    __syncthreads();
+    const int cap = n / Gk * Gk;
+    const int c_hi = min((int)((s_cnt[0] + Gk - 1) / Gk) * Gk, cap);
+    const int c_kept = max(min((int)((s_cnt[1] + Gk - 1) / Gk) * Gk, cap), c_hi);
+    // thresholds as keys: (T, need_eq) for both counts; k = 0 takes nothing
+    uint32_t need_hi = 0, need_kept = 0, T_hi = 0xffffffffu, T_kept = 0xffffffffu;
+    if (c_hi > 0) T_hi = kth_key<kSelThreads>(c, n, (uint32_t)c_hi, L, &need_hi);
+    if (c_kept > 0) T_kept = kth_key<kSelThreads>(c, n, (uint32_t)c_kept, L, &need_kept);
+    int32_t *oh = idx_hi + (size_t)unit * n;
+    int32_t *ol = idx_lo + (size_t)unit * n;
+    uint32_t base_h = 0, base_l = 0, eqh_seen = 0, eqk_seen = 0;
+    for (int t0 = 0; t0 < n; t0 += kSelThreads) {
         const int j = t0 + tid;
-        const uint32_t u = j < nc ? order_key(c[j]) : 0u;
-        const uint32_t gt = (j < nc && u > T) ? 1u : 0u;
-        const uint32_t eq = (j < nc && u == T) ? 1u : 0u;
-        uint32_t eq_tot;
-        const uint32_t eq_rank = eq_seen + block_excl_scan(eq, wsum, &eq_tot);
-        const uint32_t take = gt | (eq & (eq_rank < need_eq ? 1u : 0u));
-        uint32_t take_tot;
-        const uint32_t pos = base + block_excl_scan(take, wsum, &take_tot);
-        if (take && pos < (uint32_t)n_hh) out[pos] = j;
-        base += take_tot;
-        eq_seen += eq_tot;
+        const uint32_t u = j < n ? order_key(c[j]) : 0u;
+        const uint32_t eqh = (j < n && c_hi > 0 && u == T_hi) ? 1u : 0u;
+        const uint32_t eqk = (j < n && c_kept > 0 && u == T_kept) ? 1u : 0u;
+        uint32_t tot;
+        const uint32_t rh = eqh_seen + block_excl_scan<kSelThreads>(eqh, L.wsum, &tot);
+        eqh_seen += tot;
+        const uint32_t rk = eqk_seen + block_excl_scan<kSelThreads>(eqk, L.wsum, &tot);
+        eqk_seen += tot;
+        const bool in_hi = j < n && c_hi > 0 && (u > T_hi || (eqh && rh < need_hi));
+        const bool in_kept = j < n && c_kept > 0 && (u > T_kept || (eqk && rk < need_kept));
+        const uint32_t th = in_hi ? 1u : 0u;
+        const uint32_t tl = (in_kept && !in_hi) ? 1u : 0u;
+        const uint32_t ph = base_h + block_excl_scan<kSelThreads>(th, L.wsum, &tot);
+        base_h += tot;
+        const uint32_t pl = base_l + block_excl_scan<kSelThreads>(tl, L.wsum, &tot);
+        base_l += tot;
+        if (th && ph < (uint32_t)c_hi) oh[ph] = j;
+        if (tl && pl < (uint32_t)(c_kept - c_hi)) ol[pl] = j;
+    }
+    if (tid == 0) {
+        n_hi[unit] = c_hi;
+        n_lo[unit] = c_kept - c_hi;
     }
 }
 
@@ -144,6 +96,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 hipError_t launch_select(const float *col, int units, int n, int n_hh,
                          int n_recent, int32_t *sel, hipStream_t stream) {
     select_kernel<<<units, kSelThreads, 0, stream>>>(col, n, n_hh, n_recent, sel);
+    return hipGetLastError();
+}
+
+hipError_t launch_tier(const float *score, int units, int n, float alpha_hi,
+                       float alpha_lo, int Gk, int32_t *idx_hi, int32_t *idx_lo,
+                       int32_t *n_hi, int32_t *n_lo, hipStream_t stream) {
+    // thresholds alpha / n, one fp32 division each
+    const float thr_hi = alpha_hi / (float)n, thr_lo = alpha_lo / (float)n;
+    tier_kernel<<<units, kSelThreads, 0, stream>>>(score, n, thr_hi, thr_lo, Gk, idx_hi,
+                                                   idx_lo, n_hi, n_lo);
     return hipGetLastError();
 }
 

@@ -399,3 +399,299 @@ def decode_attn_noalloc(dims, cache, q, o=None, stream=None):
                                             ctypes.byref(cache.c), _ptr(q),
                                             _ptr(o), _stream(stream)))
     return o
+
+
+# ------------------------------------------------ mixed-precision caches --
+# MiKV (important tokens at high precision, the rest kept at low precision)
+# and DiffKV (K8V4 / K4V2 tiers by significance, pruning the rest): packed
+# segments of their own bit widths plus one fp16 residual
+# (include/minikv.h, "mixed-precision caches").
+
+MAX_SEGMENTS = 3
+
+
+class _SegC(ctypes.Structure):
+    _fields_ = [("kq", _P), ("k_scale", _P), ("k_zero", _P), ("vq", _P),
+                ("v_scale", _P), ("v_zero", _P), ("key_bits", _i32),
+                ("value_bits", _i32), ("capacity", _i32), ("n_packed", _i32),
+                ("n_unit", _P)]
+
+
+class _MixedC(ctypes.Structure):
+    _fields_ = [("seg", _SegC * MAX_SEGMENTS), ("n_seg", _i32),
+                ("flush_seg", _i32), ("k_res", _P), ("v_res", _P),
+                ("n_res", _i32)]
+
+
+_MIXED_SIG = {
+    "minikv_segment_layout": (["D", _i32, _i32, _i32, _P], _i32),
+    "minikv_mikv_ws_bytes": (["D", _i32, _i32, _P], _i32),
+    "minikv_pack_mikv": (["D", _i32, _P, _P, _P, _i32, "M", _P, _sz, _P], _i32),
+    "minikv_append_mixed": (["D", "M", _P, _P, _P], _i32),
+    "minikv_decode_mixed_ws_bytes": (["D", "M", _P], _i32),
+    "minikv_decode_mixed": (["D", "M", _P, _P, _P, _sz, _P], _i32),
+    "minikv_diffkv_ws_bytes": (["D", _i32, _i32, _P], _i32),
+    "minikv_prefill_diffkv": (["D", _i32, _P, _P, _P, _P, _P, _P, _P, _sz, _P],
+                              _i32),
+    "minikv_tier_diffkv": (["D", _i32, _P, ctypes.c_float, ctypes.c_float, _P,
+                           _P, _P, _P, _P], _i32),
+    "minikv_pack_diffkv": (["D", _i32, _P, _P, _P, _P, _P, _P, "M", _P], _i32),
+}
+EXPORTED = EXPORTED + tuple(_MIXED_SIG)
+
+
+def _mixed_lib():
+    L = lib()
+    if not getattr(L, "_mixed_sig_set", False):
+        D = ctypes.POINTER(Dims)
+        M = ctypes.POINTER(_MixedC)
+        for name, (args, res) in _MIXED_SIG.items():
+            f = getattr(L, name)
+            f.argtypes = [D if a == "D" else M if a == "M" else a for a in args]
+            f.restype = res
+        L._mixed_sig_set = True
+    return L
+
+
+def segment_layout(dims, key_bits, value_bits, capacity):
+    out = (ctypes.c_size_t * 6)()
+    _check(_mixed_lib().minikv_segment_layout(ctypes.byref(dims), key_bits,
+                                              value_bits, capacity,
+                                              ctypes.cast(out, _P)))
+    return list(out)
+
+
+class MixedCache:
+    """Device arrays of a mixed-precision cache: `segs` is a list of
+    (key_bits, value_bits, capacity); flush_seg receives residual flushes.
+    Segment i's arrays are self.seg[i][name] with
+      kq [U][key_bits/2][cap][D/16] int32, k_scale/k_zero [U][cap/Gk][D],
+      vq [U][value_bits/2][cap/16][D] int32, v_scale/v_zero [U][cap][D/Gv]."""
+
+    SEG_NAMES = ("kq", "k_scale", "k_zero", "vq", "v_scale", "v_zero")
+
+    def __init__(self, dims, segs, flush_seg=0, device="cuda"):
+        assert 1 <= len(segs) <= MAX_SEGMENTS
+        self.dims = dims
+        U, D = dims.units, dims.head_dim
+        Gk, Gv, nr = dims.group_k, dims.group_v, dims.residual_cap
+        self.c = _MixedC()
+        self.seg = []
+        for i, (kb, vb, cap) in enumerate(segs):
+            sizes = segment_layout(dims, kb, vb, cap)
+            shapes = {
+                "kq": ((U, kb // 2, cap, D // 16), torch.int32),
+                "k_scale": ((U, cap // Gk, D), torch.float16),
+                "k_zero": ((U, cap // Gk, D), torch.float16),
+                "vq": ((U, vb // 2, cap // 16, D), torch.int32),
+                "v_scale": ((U, cap, D // Gv), torch.float16),
+                "v_zero": ((U, cap, D // Gv), torch.float16),
+            }
+            arrs = {}
+            for name, nbytes in zip(self.SEG_NAMES, sizes):
+                shape, dt = shapes[name]
+                t = torch.zeros(shape, dtype=dt, device=device)
+                assert t.numel() * t.element_size() == nbytes
+                arrs[name] = t
+            self.seg.append(arrs)
+            s = self.c.seg[i]
+            for name in self.SEG_NAMES:
+                setattr(s, name, _P(arrs[name].data_ptr()))
+            s.key_bits, s.value_bits, s.capacity, s.n_packed = kb, vb, cap, 0
+            s.n_unit = None
+        self.c.n_seg = len(segs)
+        self.c.flush_seg = flush_seg
+        self.k_res = torch.zeros((U, nr, D), dtype=torch.float16, device=device)
+        self.v_res = torch.zeros_like(self.k_res)
+        self.c.k_res = _P(self.k_res.data_ptr())
+        self.c.v_res = _P(self.v_res.data_ptr())
+        self.c.n_res = 0
+        self._keep = []                      # device count arrays in use
+
+    @property
+    def n_res(self):
+        return self.c.n_res
+
+    def n_packed(self, i):
+        return self.c.seg[i].n_packed
+
+    def set_bound(self, i, bound):
+        """Lower segment i's packed-token bound (e.g. to the largest
+        per-unit count after reading the counts back)."""
+        self.c.seg[i].n_packed = int(bound)
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for s in self.seg for t in s.values()) + \
+            2 * self.k_res.numel() * 2
+
+
+def mikv_ws_bytes(dims, n, n_sel):
+    out = ctypes.c_size_t()
+    _check(_mixed_lib().minikv_mikv_ws_bytes(ctypes.byref(dims), n, n_sel,
+                                             ctypes.cast(ctypes.pointer(out), _P)))
+    return out.value
+
+
+def pack_mikv(dims, k, v, sel, cache, ws=None, stream=None):
+    """MiKV pack: sel (the important tokens) into segment 0, the other
+    tokens into segment 1, tails to the fp16 residual."""
+    B, Hkv, D = dims.batch, dims.n_kv_heads, dims.head_dim
+    n = k.shape[2]
+    _need(k, torch.float16, (B, Hkv, n, D), "k")
+    _need(v, torch.float16, (B, Hkv, n, D), "v")
+    n_sel = sel.shape[-1]
+    _need(sel, torch.int32, (B, Hkv, n_sel), "sel")
+    need = mikv_ws_bytes(dims, n, n_sel)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+    ws_bytes = _ws(ws, need)
+    _check(_mixed_lib().minikv_pack_mikv(
+        ctypes.byref(dims), n, _ptr(k), _ptr(v), _ptr(sel), n_sel,
+        ctypes.byref(cache.c), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def append_mixed(dims, cache, k_new, v_new, stream=None):
+    shape = (dims.batch, dims.n_kv_heads, dims.head_dim)
+    _need(k_new, torch.float16, shape, "k_new")
+    _need(v_new, torch.float16, shape, "v_new")
+    _check(_mixed_lib().minikv_append_mixed(ctypes.byref(dims),
+                                            ctypes.byref(cache.c), _ptr(k_new),
+                                            _ptr(v_new), _stream(stream)))
+
+
+def decode_mixed_ws_bytes(dims, cache):
+    out = ctypes.c_size_t()
+    _check(_mixed_lib().minikv_decode_mixed_ws_bytes(
+        ctypes.byref(dims), ctypes.byref(cache.c),
+        ctypes.cast(ctypes.pointer(out), _P)))
+    return out.value
+
+
+def decode_mixed(dims, cache, q, o=None, ws=None, stream=None):
+    shape = (dims.batch, dims.n_q_heads, dims.head_dim)
+    _need(q, torch.float16, shape, "q")
+    o = _out(o, torch.float16, shape, "o", q)
+    need = decode_mixed_ws_bytes(dims, cache)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = _ws(ws, need)
+    _check(_mixed_lib().minikv_decode_mixed(ctypes.byref(dims),
+                                            ctypes.byref(cache.c), _ptr(q),
+                                            _ptr(o), _ptr(ws), ws_bytes,
+                                            _stream(stream)))
+    return o
+
+
+def prefill_diffkv(dims, q, k, v, o=None, score=None, lse=None, ws=None,
+                   stream=None):
+    """Prefill attention plus DiffKV's per-key significance [B][Hkv][n]."""
+    B, Hq, Hkv, D = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    n = q.shape[2]
+    _need(q, torch.float16, (B, Hq, n, D), "q")
+    _need(k, torch.float16, (B, Hkv, n, D), "k")
+    _need(v, torch.float16, (B, Hkv, n, D), "v")
+    o = _out(o, torch.float16, (B, Hq, n, D), "o", q)
+    score = _out(score, torch.float32, (B, Hkv, n), "score", q)
+    ws_bytes = 0
+    if lse is not None:
+        _need(lse, torch.float32, (B, Hq, n), "lse")
+    elif ws is None:
+        ws = torch.empty(prefill_ws_bytes(dims, n), dtype=torch.uint8,
+                         device=q.device)
+    if ws is not None:
+        ws_bytes = _ws(ws, 0 if lse is not None else prefill_ws_bytes(dims, n))
+    _check(_mixed_lib().minikv_prefill_diffkv(
+        ctypes.byref(dims), n, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(score),
+        _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+    return o, score
+
+
+def tier_diffkv(dims, score, alpha_hi, alpha_lo, idx_hi=None, idx_lo=None,
+                n_hi=None, n_lo=None, stream=None):
+    """DiffKV tiers: (idx_hi, idx_lo [B][Hkv][n], n_hi, n_lo [B*Hkv])."""
+    B, Hkv = dims.batch, dims.n_kv_heads
+    n = score.shape[-1]
+    _need(score, torch.float32, (B, Hkv, n), "score")
+    idx_hi = _out(idx_hi, torch.int32, (B, Hkv, n), "idx_hi", score)
+    idx_lo = _out(idx_lo, torch.int32, (B, Hkv, n), "idx_lo", score)
+    n_hi = _out(n_hi, torch.int32, (B * Hkv,), "n_hi", score)
+    n_lo = _out(n_lo, torch.int32, (B * Hkv,), "n_lo", score)
+    _check(_mixed_lib().minikv_tier_diffkv(
+        ctypes.byref(dims), n, _ptr(score), float(alpha_hi), float(alpha_lo),
+        _ptr(idx_hi), _ptr(idx_lo), _ptr(n_hi), _ptr(n_lo), _stream(stream)))
+    return idx_hi, idx_lo, n_hi, n_lo
+
+
+def pack_diffkv(dims, k, v, idx_hi, idx_lo, n_hi, n_lo, cache, stream=None):
+    """DiffKV pack into a three-segment cache (K8V4 tier, K4V2 tier,
+    generated tokens at K8V4); the count arrays stay referenced by the
+    cache."""
+    B, Hkv, D = dims.batch, dims.n_kv_heads, dims.head_dim
+    n = k.shape[2]
+    _need(k, torch.float16, (B, Hkv, n, D), "k")
+    _need(v, torch.float16, (B, Hkv, n, D), "v")
+    for t, name in ((idx_hi, "idx_hi"), (idx_lo, "idx_lo")):
+        _need(t, torch.int32, (B, Hkv, n), name)
+    for t, name in ((n_hi, "n_hi"), (n_lo, "n_lo")):
+        _need(t, torch.int32, (B * Hkv,), name)
+    _check(_mixed_lib().minikv_pack_diffkv(
+        ctypes.byref(dims), n, _ptr(k), _ptr(v), _ptr(idx_hi), _ptr(idx_lo),
+        _ptr(n_hi), _ptr(n_lo), ctypes.byref(cache.c), _stream(stream)))
+    cache._keep = [n_hi, n_lo]
+
+
+# ------------------------------------------------------ fused prefill tail --
+
+_TAIL_SIG = {
+    "minikv_prefill_tail_ws_bytes": (["D", _i32, _i32, _P], _i32),
+    "minikv_prefill_select_pack": (["D", _i32, _P, _P, _P, _P, _P, _P, _i32, _i32,
+                                    _P, "C", _i32, _P, _sz, _P], _i32),
+}
+EXPORTED = EXPORTED + tuple(_TAIL_SIG)
+
+
+def _tail_lib():
+    L = lib()
+    if not getattr(L, "_tail_sig_set", False):
+        D = ctypes.POINTER(Dims)
+        C = ctypes.POINTER(_CacheC)
+        for name, (args, res) in _TAIL_SIG.items():
+            f = getattr(L, name)
+            f.argtypes = [D if a == "D" else C if a == "C" else a for a in args]
+            f.restype = res
+        L._tail_sig_set = True
+    return L
+
+
+def prefill_tail_ws_bytes(dims, n, lse_given=False):
+    out = ctypes.c_size_t()
+    _check(_tail_lib().minikv_prefill_tail_ws_bytes(
+        ctypes.byref(dims), n, 1 if lse_given else 0,
+        ctypes.cast(ctypes.pointer(out), _P)))
+    return out.value
+
+
+def prefill_select_pack(dims, q, k, v, n_hh, n_recent, cache, fuse_select=False,
+                        o=None, col=None, lse=None, sel=None, ws=None,
+                        stream=None):
+    """prefill_select then pack in one call, the selection fused into the
+    second prefill pass when fuse_select; returns (o, col, sel)."""
+    B, Hq, Hkv, D = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    n = q.shape[2]
+    _need(q, torch.float16, (B, Hq, n, D), "q")
+    _need(k, torch.float16, (B, Hkv, n, D), "k")
+    _need(v, torch.float16, (B, Hkv, n, D), "v")
+    o = _out(o, torch.float16, (B, Hq, n, D), "o", q)
+    col = _out(col, torch.float32, (B, Hkv, n), "col", q)
+    sel = _out(sel, torch.int32, (B, Hkv, n_hh + n_recent), "sel", q)
+    if lse is not None:
+        _need(lse, torch.float32, (B, Hq, n), "lse")
+    need = prefill_tail_ws_bytes(dims, n, lse is not None)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = _ws(ws, need)
+    _check(_tail_lib().minikv_prefill_select_pack(
+        ctypes.byref(dims), n, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(col),
+        _ptr(lse), n_hh, n_recent, _ptr(sel), ctypes.byref(cache.c),
+        1 if fuse_select else 0, _ptr(ws), ws_bytes, _stream(stream)))
+    return o, col, sel

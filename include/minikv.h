@@ -297,6 +297,199 @@ MINIKV_API int32_t minikv_decode_attn_mass(const minikv_dims *dims,
                                            int32_t mass_stride, void *ws,
                                            size_t ws_bytes, void *stream);
 
+/* ================================================== fused prefill tail
+ *
+ * The prefill phase's own cost (the Pith review's referee report names a
+ * prefill-phase slowdown) ends with a selection and a pack after the two
+ * attention passes.  minikv_prefill_select_pack runs the whole tail in one
+ * call.  With fuse_select = 1 the heavy-hitter + recent-window selection of
+ * a unit runs inside the second pass, in the last workgroup to finish that
+ * unit's key columns (no separate selection launch; a unit's selection can
+ * overlap the other units' second pass); with 0 the selection kernel runs
+ * after the second pass.  The pack of every unit follows.  Either way the
+ * results are those of minikv_prefill_select followed by minikv_pack with
+ * the same sel, bit for bit.  On MI355X the units of a layer finish their
+ * second pass together, so the fused selection (one 256-thread workgroup
+ * per unit) lands on the critical path: measured 6% slower at 4096 tokens
+ * and equal at 32768 and 131072; 0 is the faster choice there. */
+
+/* Workspace bytes of minikv_prefill_select_pack: the LSE when lse is NULL
+ * (lse_given = 0), then one 32-bit completion counter per unit. */
+MINIKV_API int32_t minikv_prefill_tail_ws_bytes(const minikv_dims *dims, int32_t n,
+                                                int32_t lse_given, size_t *out);
+
+/* Prefill attention, selection and pack of one layer (see above).
+ * Arguments as for minikv_prefill_select and minikv_pack (sel: n_hh +
+ * n_recent indices per unit, written, then packed into `cache`); ws is
+ * required (the counters).  fuse_select: 1 fused, 0 separate (EINVAL
+ * otherwise).  Sets cache->n_packed and n_res.  ECAPACITY, with no side
+ * effect, if the selection does not fit the cache. */
+MINIKV_API int32_t minikv_prefill_select_pack(const minikv_dims *dims, int32_t n,
+                                              const void *q, const void *k,
+                                              const void *v, void *o, float *col,
+                                              float *lse, int32_t n_hh,
+                                              int32_t n_recent, int32_t *sel,
+                                              minikv_layer_cache *cache,
+                                              int32_t fuse_select, void *ws,
+                                              size_t ws_bytes, void *stream);
+
+/* ============================================== mixed-precision caches
+ *
+ * Two neighbours of MiniKV on the same pages keep more than one precision
+ * in one layer's cache:
+ *  - MiKV ("Don't Discard, but Keep It Small: Context-Preserving KV Cache
+ *    Compression with Importance-Aware Adaptive Precision", the authors'
+ *    responses [W1] and, on the implementation, [W2]): the tokens an
+ *    eviction policy would drop are kept at low precision and the important
+ *    ones at high precision; the pairs are regrouped by precision (attention
+ *    does not depend on the order of the cached pairs), each group stored
+ *    contiguously and attended with its own INTn x FP16 product.
+ *  - DiffKV (pith.science verdict record for arXiv 2412.03131,
+ *    key_machinery and core_discovery): keys get more bits than values;
+ *    tokens whose significance (the average attention they receive from
+ *    later tokens, max over a GQA group's query heads) exceeds alpha_h / N
+ *    are kept at K8V4, those above alpha_l / N at K4V2, the rest pruned,
+ *    decided per kv head.
+ *
+ * A mixed cache holds up to MINIKV_MAX_SEGMENTS packed segments plus one
+ * fp16 residual.  Segment codes of b bits are stored as b/2 planes of 2-bit
+ * codes; plane p holds bits 2p..2p+1 of every code, each plane in exactly
+ * the kq / vq word layout of minikv_layer_cache, plane-major within a unit:
+ *   kq      int32 [B][Hkv][key_bits/2][cap][D/16]
+ *   k_scale, k_zero fp16 [B][Hkv][cap/Gk][D]
+ *   vq      int32 [B][Hkv][value_bits/2][cap/16][D]
+ *   v_scale, v_zero fp16 [B][Hkv][cap][D/Gv]
+ * Codec of a b-bit group: scale = fp16((max - min) / (2^b - 1)), zero =
+ * min, code = the integer nearest to (x - zero) / scale, ties to even,
+ * clamped to [0, 2^b - 1].  (key_bits, value_bits) is one of (2, 2),
+ * (4, 4), (4, 2), (8, 4).  Mixed-cache calls need group_v == 16.
+ *
+ * n_packed is the host-side count of packed tokens per unit; when n_unit
+ * (device int32 [B*Hkv]) is set, each unit holds its own count n_unit[u]
+ * (a multiple of Gk) and n_packed is an upper bound of them (the decode
+ * grid covers n_packed; a caller that reads the counts back may lower it to
+ * their maximum).  Decode attends over every segment's packed tokens and
+ * the n_res residual tokens in one softmax.  flush_seg names the segment
+ * that receives residual flushes; it must not use n_unit. */
+#define MINIKV_MAX_SEGMENTS 3
+
+typedef struct minikv_segment {
+    int32_t *kq;
+    uint16_t *k_scale;
+    uint16_t *k_zero;
+    int32_t *vq;
+    uint16_t *v_scale;
+    uint16_t *v_zero;
+    int32_t key_bits;
+    int32_t value_bits;
+    int32_t capacity;
+    int32_t n_packed;
+    int32_t *n_unit;
+} minikv_segment;
+
+typedef struct minikv_mixed_cache {
+    minikv_segment seg[MINIKV_MAX_SEGMENTS];
+    int32_t n_seg;
+    int32_t flush_seg;
+    uint16_t *k_res;
+    uint16_t *v_res;
+    int32_t n_res;
+} minikv_mixed_cache;
+
+/* Byte sizes of a segment's six device arrays (kq, k_scale, k_zero, vq,
+ * v_scale, v_zero) for `capacity` packed tokens per unit.  EINVAL if the
+ * bit widths are not a supported pair or capacity is not a non-negative
+ * multiple of Gk. */
+MINIKV_API int32_t minikv_segment_layout(const minikv_dims *dims, int32_t key_bits,
+                                         int32_t value_bits, int32_t capacity,
+                                         size_t out_bytes[6]);
+
+/* Workspace bytes of minikv_pack_mikv: the unselected tokens' indices. */
+MINIKV_API int32_t minikv_mikv_ws_bytes(const minikv_dims *dims, int32_t n,
+                                        int32_t n_sel, size_t *out);
+
+/* MiKV pack (see above): the n_sel selected tokens of every unit (sel as for
+ * minikv_pack: ascending, in [0, n); e.g. the heavy hitters and recent
+ * window of minikv_prefill_select, H2O's policy, which MiKV's experiments
+ * use) go to seg[0], the other n - n_sel tokens, ascending, to seg[1], each
+ * at its own bit widths (MiKV's average of 3 bits: seg[0] INT4 keys and
+ * values, seg[1] INT2).  Each segment takes whole key groups; the
+ * remaining n_sel mod Gk selected tokens and then the (n - n_sel) mod Gk
+ * unselected ones stay fp16 as residual slots 0 .. n_res - 1.  Needs
+ * n_seg == 2, flush_seg == 0 (generated tokens join the high-precision
+ * segment), no n_unit.  Sets both segments' n_packed and n_res.
+ * ws: minikv_mikv_ws_bytes bytes.  ECAPACITY, with no side effect, if a
+ * segment or the residual would overflow. */
+MINIKV_API int32_t minikv_pack_mikv(const minikv_dims *dims, int32_t n, const void *k,
+                                    const void *v, const int32_t *sel, int32_t n_sel,
+                                    minikv_mixed_cache *cache, void *ws,
+                                    size_t ws_bytes, void *stream);
+
+/* minikv_append for a mixed cache: the flush packs the residual onto the
+ * end of seg[flush_seg] at that segment's bit widths. */
+MINIKV_API int32_t minikv_append_mixed(const minikv_dims *dims,
+                                       minikv_mixed_cache *cache,
+                                       const void *k_new, const void *v_new,
+                                       void *stream);
+
+/* Workspace bytes of minikv_decode_mixed for this cache's segments (from
+ * their capacities). */
+MINIKV_API int32_t minikv_decode_mixed_ws_bytes(const minikv_dims *dims,
+                                                const minikv_mixed_cache *cache,
+                                                size_t *out);
+
+/* Decode attention over a mixed cache: o[b][hq] = softmax over every packed
+ * token of every segment and the residual tokens of unit (b, hq / g), the
+ * codes of each segment dequantised in registers at its own bit widths.
+ * q, o fp16 [B][Hq][D].  EINVAL if the cache holds no token. */
+MINIKV_API int32_t minikv_decode_mixed(const minikv_dims *dims,
+                                       const minikv_mixed_cache *cache,
+                                       const void *q, void *o, void *ws,
+                                       size_t ws_bytes, void *stream);
+
+/* Workspace bytes of minikv_prefill_diffkv (the LSE, 0 when given). */
+MINIKV_API int32_t minikv_diffkv_ws_bytes(const minikv_dims *dims, int32_t n,
+                                          int32_t lse_given, size_t *out);
+
+/* DiffKV prefill: the attention output and LSE of minikv_prefill_attn, and
+ * every prompt token's significance
+ *   score[b][kvh][j] = max over the g query heads h of kv head kvh of
+ *                      (sum over rows i >= j of P[h][i][j]) / (n - j),
+ * fp32 [B][Hkv][n] (the per-head column sum, then one fp32 division).
+ * lse may be NULL when ws holds minikv_diffkv_ws_bytes bytes. */
+MINIKV_API int32_t minikv_prefill_diffkv(const minikv_dims *dims, int32_t n,
+                                         const void *q, const void *k, const void *v,
+                                         void *o, float *score, float *lse, void *ws,
+                                         size_t ws_bytes, void *stream);
+
+/* DiffKV tiers of every unit from its significance scores, thresholds
+ * thr = alpha / n in fp32 (one division): c_hi = the count of scores above
+ * alpha_hi / n and c_kept = the count above alpha_lo / n, each rounded up
+ * to a multiple of Gk (at most floor(n / Gk) * Gk; c_kept >= c_hi).  The
+ * high tier is the first c_hi tokens by (score descending, index
+ * ascending), the low tier the next c_kept - c_hi; the others are pruned.
+ *   idx_hi, idx_lo int32 [B][Hkv][n]: each tier ascending in its first
+ *                  n_hi[u] / n_lo[u] entries
+ *   n_hi, n_lo     int32 [B*Hkv] (device)
+ * alpha_lo <= alpha_hi. */
+MINIKV_API int32_t minikv_tier_diffkv(const minikv_dims *dims, int32_t n,
+                                      const float *score, float alpha_hi,
+                                      float alpha_lo, int32_t *idx_hi,
+                                      int32_t *idx_lo, int32_t *n_hi,
+                                      int32_t *n_lo, void *stream);
+
+/* DiffKV pack: the high tier into seg[0] (key_bits 8, value_bits 4) and the
+ * low tier into seg[1] (4, 2), with per-unit counts: sets seg[0].n_unit =
+ * n_hi, seg[1].n_unit = n_lo and both n_packed to floor(n / Gk) * Gk (the
+ * bound).  seg[2] (8, 4, no n_unit) receives the generated tokens
+ * (flush_seg == 2); its n_packed and n_res are set to 0.  Needs n_seg == 3
+ * and each tier segment's capacity >= floor(n / Gk) * Gk. */
+MINIKV_API int32_t minikv_pack_diffkv(const minikv_dims *dims, int32_t n, const void *k,
+                                      const void *v, const int32_t *idx_hi,
+                                      const int32_t *idx_lo, int32_t *n_hi,
+                                      int32_t *n_lo, minikv_mixed_cache *cache,
+                                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif
