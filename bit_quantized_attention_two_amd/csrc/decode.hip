@@ -16,11 +16,14 @@
 // Masking a word with 0x00030003 << 2i leaves two 2-bit fields in the
 // mantissas of two fp16 halves: the subnormals code * 4^i * 2^-24, exact.
 // The matching weights (q s for keys, p s for values) are scaled by 4^-i and
-// split into two fp16 parts hi + lo, which hold the fp32 weight to about 22
-// bits; each product code * weight is exact in the fp32 accumulator.  So the
-// only rounding is the fp32 accumulation, as in a plain fp32 dot product.
-// Every fp16 operand stays within range: q is scaled by a power of two to
-// |q| < 1 per head, p <= 1, and a scale is at most 65504 * 2 / 3.
+// split into two fp16 parts hi + lo, which hold the weight to 2^-25
+// absolute (to about 22 bits where lo is a normal fp16); each product code *
+// weight is exact in the fp32 accumulator, so the other rounding is the fp32
+// accumulation, as in a plain fp32 dot product.  Key weights: q is scaled per
+// head by 2^-e (|q| < 1) and per slot by 4^-i once, in fp16 (exact unless
+// subnormal), and each weight is the exact TwoProduct hi + lo of that q and
+// the fp16 scale.  Value weights: the fp32 product p s, split.  Every fp16
+// operand stays within range: p <= 1, and a scale is at most 65504 * 2 / 3.
 //
 // The per-group scale s_k[g, c] makes the key weights differ per key group.
 // One 16-column B operand holds the weights of (head, group) pairs for 16/g
@@ -103,9 +106,48 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp<0x121>(v);       // row_ror:1
     return v;
 }
+// The values of lane l and lane l ^ 16 (or l ^ 32) in every lane:
+// v_permlane16_swap / v_permlane32_swap with both operands x return them as
+// the two result elements (the copy is hidden from the compiler so that the
+// swap of a value with itself is not folded).  Used with symmetric
+// operations only, so which element is which does not matter.
+__device__ __forceinline__ float xor16_sum(float x) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    asm volatile("" : "+v"(b));
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    asm volatile("" : "+v"(b));
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    asm volatile("" : "+v"(b));
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    asm volatile("" : "+v"(b));
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+// Sum over the wave, in every lane (the same value in each: every step adds
+// a lane pair's two values, which both lanes of the pair hold alike).
 __device__ __forceinline__ float wave_sum(float v) {
-    for (int off = 32; off > 0; off >>= 1) v += shfl_xor(v, off);
-    return v;
+    return xor32_sum(xor16_sum(row16_sum(v)));
+}
+// Max over the lanes l' with l' = l (mod S) in every lane l, S | 16.
+template <int S>
+__device__ __forceinline__ float strided_max(float m) {
+    if constexpr (S <= 1) m = fmaxf(m, dpp<0x121>(m));    // row_ror:1
+    if constexpr (S <= 2) m = fmaxf(m, dpp<0x122>(m));    // row_ror:2
+    if constexpr (S <= 4) m = fmaxf(m, dpp<0x124>(m));    // row_ror:4
+    if constexpr (S <= 8) m = fmaxf(m, dpp<0x128>(m));    // row_ror:8
+    return xor32_max(xor16_max(m));
 }
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
@@ -133,16 +175,38 @@ __device__ __forceinline__ half8_t code_operand2(uint32_t x0, uint32_t x1) {
 }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-// fp16 hi + lo of two weights: hi truncated (one v_cvt_pkrtz for both), lo
-// the rest w - hi, exact in fp32, rounded to fp16.  hi + lo holds w to
-// about 22 bits.
+// fp16 hi + lo of two fp32 weights: hi truncated (one v_cvt_pkrtz for both),
+// lo the rest w - hi, exact in fp32, rounded to fp16 (one mixed-precision
+// FMA per weight, written into its half: the compiler would otherwise widen
+// hi, subtract and repack).  hi + lo holds w to 2^-25 absolute, and to about
+// 22 bits where lo stays in fp16's normal range.
 __device__ __forceinline__ void split2x2(float w0, float w1, uint32_t &hi, uint32_t &lo) {
-    const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(w0, w1));
-    // w - hi in one mixed-precision FMA each (v_fma_mix{lo,hi}_f16)
-    const half2_t l = {(half_t)__builtin_fmaf((float)h[0], -1.f, w0),
-                       (half_t)__builtin_fmaf((float)h[1], -1.f, w1)};
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w0, w1));
+    uint32_t l;
+    asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(l) : "v"(h), "s"(-1.0f), "v"(w0));
+    asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "+v"(l) : "v"(h), "s"(-1.0f), "v"(w1));
+    hi = h;
+    lo = l;
+}
+
+// hi + lo = a * b for fp16 pairs (TwoProduct with a fused fp16 FMA): hi is
+// the rounded product, lo = a b - hi rounded once, exact while it stays in
+// fp16's normal range, else within 2^-25.
+__device__ __forceinline__ void two_product2(uint32_t a, uint32_t b, uint32_t &hi, uint32_t &lo) {
+    const half2_t x = __builtin_bit_cast(half2_t, a), y = __builtin_bit_cast(half2_t, b);
+    const half2_t h = x * y;
     hi = __builtin_bit_cast(uint32_t, h);
-    lo = __builtin_bit_cast(uint32_t, l);
+    lo = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(x, y, -h));
+}
+
+// The fp16 pair (low half of a, low half of b), and (high half of a, high
+// half of b).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 __device__ __forceinline__ void unpack8h(uint4 x, float *f) {
@@ -210,6 +274,8 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, qd = lane >> 4;
     const int Gk = c.Gk;
+    const int gk_sh = __builtin_ctz(Gk);          // Gk is a power of two
+    constexpr int NG_SH = G == 1 ? 4 : G == 2 ? 3 : G == 4 ? 2 : 1;   // log2(16 / G)
     const int NGV = D / c.Gv;                     // stored value groups
     const uint16_t *qu = a.q + (size_t)unit * G * D;
     const uint32_t *kq = reinterpret_cast<const uint32_t *>(c.kq) +
@@ -221,10 +287,11 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                          (size_t)unit * c.vq_unit();
     const uint16_t *vs = c.vs + (size_t)unit * c.vm_unit();
     const uint16_t *vz = c.vz + (size_t)unit * c.vm_unit();
-    const int g_first = t0 / Gk;
-    const int n_grp = nt / Gk;
+    const int g_first = t0 >> gk_sh;
+    const int n_grp = nt >> gk_sh;
     const int nbatch = (nt + BT - 1) / BT;
-    const int bblk = NG * Gk;                     // tokens per key B operand
+    const int bb_sh = NG_SH + gk_sh;
+    const int bblk = 1 << bb_sh;                  // tokens per key B operand (NG Gk)
     const int last = (nbatch - 1) * BT;           // start of the last batch
 
     // ---- key B operand columns: column r = (group r / G of the operand,
@@ -234,8 +301,8 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     const int gcol = r / G;
 
     // ---- this lane's q channels as fp16 pairs (hf = 0, 1) per (kb, i), in
-    // the k-slot order of the key operands; and the power of two
-    // 2^e > max |q_h| per head.
+    // the k-slot order of the key operands; the power of two 2^e > max |q_h|
+    // per head; then q 2^(-e-2i) in place.
     uint32_t qh[KB][4];
     float qmax = 0.f;
 #pragma unroll
@@ -254,17 +321,28 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             qmax = fmaxf(qmax, fmaxf(fabsf(h2f((uint16_t)lo)), fabsf(h2f((uint16_t)hi))));
         }
     }
-    qmax = fmaxf(qmax, shfl_xor(qmax, 16));
-    qmax = fmaxf(qmax, shfl_xor(qmax, 32));
-    const int qe = __builtin_amdgcn_frexp_expf(qmax);
+    qmax = xor32_max(xor16_max(qmax));
+    // any e with 2^e > max |q| keeps |q 2^-e| < 1; e >= -8 keeps the factors
+    // 2^(-e-2i) within fp16
+    const int qe = max(__builtin_amdgcn_frexp_expf(qmax), -8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half_t f = (half_t)__builtin_amdgcn_ldexpf(1.f, -qe - 2 * i);   // exact
+        const half2_t ff = {f, f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            qh[kb][i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, qh[kb][i]) * ff);
+    }
     // logit (log2 units) = (acc * 2^(24 + e) + z term) * qscale
     const float kfac = __builtin_amdgcn_ldexpf(a.qscale, 24 + qe);
+    // the z terms' MFMA takes z 4^(i-3) against q 2^(-e-2i)
+    const float zfac = __builtin_amdgcn_ldexpf(a.qscale, 6 + qe);
 
 
     // ---- loaders (indices clamped, never predicated)
     uint2 ksr[KB][2];                             // key scales of a B operand
     auto load_kscale = [&](int tok) {             // B operand holding tok
-        const int gs = g_first + min((tok / bblk) * NG + gcol, n_grp - 1);
+        const int gs = g_first + min(((tok >> bb_sh) << NG_SH) + gcol, n_grp - 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int w = (qd >> 1) * KB + kb;
@@ -276,7 +354,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     };
     uint2 kzr[KB][2];                             // key zeros, rows = groups
     auto load_kzero = [&](int tok) {
-        const int gz = g_first + min((tok / bblk) * NG + r, n_grp - 1);
+        const int gz = g_first + min(((tok >> bb_sh) << NG_SH) + r, n_grp - 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int w = (qd >> 1) * KB + kb;
@@ -286,51 +364,49 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                     kz + (size_t)gz * D + 16 * w + 4 * (qd & 1) + 8 * hf);
         }
     };
-    uint32_t kw[KP][TPB][KB];                     // key words of a batch
-    auto load_kwords = [&](int tok) {
+    typedef uint32_t KWords[KP][TPB][KB];         // key words of a batch
+    KWords kw;
+    // tile j's words of the batch at tok
+    auto load_ktile = [&](int tok, int j, KWords &kw) {
+        const int t = min(tok + 16 * j + r, nt - 1);
 #pragma unroll
-        for (int j = 0; j < TPB; ++j) {
-            const int t = min(tok + 16 * j + r, nt - 1);
-#pragma unroll
-            for (int pl = 0; pl < KP; ++pl) {
-                const uint32_t *wp = kq + pl * kpl + (uint32_t)((t0 + t) * KW + (qd >> 1) * KB);
-                if constexpr (KB == 4) {
-                    const uint4 x = *reinterpret_cast<const uint4 *>(wp);
-                    kw[pl][j][0] = x.x; kw[pl][j][1] = x.y; kw[pl][j][2] = x.z; kw[pl][j][3] = x.w;
-                } else {
-                    const uint2 x = *reinterpret_cast<const uint2 *>(wp);
-                    kw[pl][j][0] = x.x; kw[pl][j][1] = x.y;
-                }
+        for (int pl = 0; pl < KP; ++pl) {
+            const uint32_t *wp = kq + pl * kpl + (uint32_t)((t0 + t) * KW + (qd >> 1) * KB);
+            if constexpr (KB == 4) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(wp);
+                kw[pl][j][0] = x.x; kw[pl][j][1] = x.y; kw[pl][j][2] = x.z; kw[pl][j][3] = x.w;
+            } else {
+                const uint2 x = *reinterpret_cast<const uint2 *>(wp);
+                kw[pl][j][0] = x.x; kw[pl][j][1] = x.y;
             }
         }
     };
+    auto load_kwords = [&](int tok, KWords &kw) {
+#pragma unroll
+        for (int j = 0; j < TPB; ++j) load_ktile(tok, j, kw);
+    };
     // the key code operand of tile j, k-block kb, from planes pl, pl + 1
-    auto key_operand = [&](int j, int kb, int pl) -> half8_t {
+    auto key_operand = [&](const KWords &kw, int j, int kb, int pl) -> half8_t {
         const int sh = 8 * (qd & 1);
         if constexpr (KP == 1) return code_operand(kw[0][j][kb] >> sh);
         else return code_operand2(kw[pl][j][kb] >> sh, kw[pl + 1][j][kb] >> sh);
     };
 
-    // key weights (B operand) from the scales in ksr
+    // key weights (B operand) from the scales in ksr: slot (i, hf) pairs the
+    // scales of channels c + i and c + 8 + i, the halves of qh[kb][i]
     half8_t bhi[KB], blo[KB];
     auto build_b = [&]() {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const uint32_t sx[2][2] = {{ksr[kb][0].x, ksr[kb][0].y},
-                                       {ksr[kb][1].x, ksr[kb][1].y}};
+            const uint32_t sp[4] = {pair_lo(ksr[kb][0].x, ksr[kb][1].x),
+                                    pair_hi(ksr[kb][0].x, ksr[kb][1].x),
+                                    pair_lo(ksr[kb][0].y, ksr[kb][1].y),
+                                    pair_hi(ksr[kb][0].y, ksr[kb][1].y)};
             u32x4 hw, lw;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float w[2];
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const half_t sc = __builtin_bit_cast(half_t, (uint16_t)(sx[hf][i >> 1] >> (16 * (i & 1))));
-                    const half_t qv = __builtin_bit_cast(half_t, (uint16_t)(qh[kb][i] >> (16 * hf)));
-                    // exact fp16 x fp16 product (v_fma_mix_f32), then 2^-e 4^-i
-                    w[hf] = __builtin_amdgcn_ldexpf(__builtin_fmaf((float)qv, (float)sc, 0.f), -qe - 2 * i);
-                }
                 uint32_t h_, l_;
-                split2x2(w[0], w[1], h_, l_);
+                two_product2(qh[kb][i], sp[i], h_, l_);
                 hw[i] = h_;
                 lw[i] = l_;
             }
@@ -339,21 +415,31 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         }
     };
     // z terms of the operand's groups (rows) for every head (columns), in
-    // log2 units, with the key operands' channel order on both sides
+    // log2 units, with the key operands' channel order on both sides: z
+    // 4^(i-3) (exact unless subnormal; never larger than z) against q
+    // 2^(-e-2i), so every product is z q 2^(-e-6)
     auto build_bias = [&]() {
         float4_t cb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const u32x4 zb = {(kzr[kb][0].x & 0xffffu) | (kzr[kb][1].x << 16),
-                              (kzr[kb][0].x >> 16) | (kzr[kb][1].x & 0xffff0000u),
-                              (kzr[kb][0].y & 0xffffu) | (kzr[kb][1].y << 16),
-                              (kzr[kb][0].y >> 16) | (kzr[kb][1].y & 0xffff0000u)};
+            const uint32_t zp[4] = {pair_lo(kzr[kb][0].x, kzr[kb][1].x),
+                                    pair_hi(kzr[kb][0].x, kzr[kb][1].x),
+                                    pair_lo(kzr[kb][0].y, kzr[kb][1].y),
+                                    pair_hi(kzr[kb][0].y, kzr[kb][1].y)};
+            u32x4 zb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const half_t f = (half_t)(1.f / (float)(1 << (6 - 2 * i)));
+                const half2_t ff = {f, f};
+                zb[i] = i == 3 ? zp[i]
+                               : __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, zp[i]) * ff);
+            }
             const u32x4 qv = {qh[kb][0], qh[kb][1], qh[kb][2], qh[kb][3]};
             cb = mfma16(__builtin_bit_cast(half8_t, zb), __builtin_bit_cast(half8_t, qv), cb);
         }
         if (r < G)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) L.bias[(4 * qd + i) * G + r] = cb[i] * a.qscale;
+            for (int i = 0; i < 4; ++i) L.bias[(4 * qd + i) * G + r] = cb[i] * zfac;
     };
 
     // value meta of the lane's token lane + 64 k (indices clamped)
@@ -415,7 +501,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     load_kscale(0);
     load_kzero(0);
     __builtin_amdgcn_sched_barrier(0);
-    load_kwords(0);
+    load_kwords(0, kw);
     __builtin_amdgcn_sched_barrier(0);
     constexpr int NVE = ONE ? 2 : 1;              // value steps held early
     uint32_t vwe[NPASS][NVE][MBP * VP];
@@ -434,18 +520,32 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         wave_lds_sync();
     }
     float mloc = -INFINITY;
-    // g = 1 with 16-token key groups: the key operand's column T belongs to
-    // the wave's tile T, so each lane keeps the accumulator of its own
-    // column's tile (a select per tile) and the logit epilogue runs once
-    // after the key phase instead of once per tile on a sixteenth of the
-    // lanes.
-    const bool per_lane = G == 1 && Gk == 16;     // uniform
+    // With 16-token key groups, column group T of a key operand belongs to
+    // the operand's tile T, so each lane keeps the accumulator of its own
+    // column's tile (a select per tile) and the logit epilogue runs once per
+    // operand on every lane instead of once per tile on a fraction of them.
+    const bool per_lane = Gk == 16;               // uniform
     float4_t keep = {0.f, 0.f, 0.f, 0.f};
+    auto store_logits = [&](const float4_t &acc, float bz, int tt) {
+        float4_t lg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lg[i] = __builtin_fmaf(acc[i], kfac, bz);
+            mloc = fmaxf(mloc, lg[i]);
+        }
+        *reinterpret_cast<float4_t *>(&L.ls[hk * kLsStride + tt + 4 * qd]) = lg;
+        if constexpr (MASS)                       // the mass audit's logits
+            *reinterpret_cast<float4_t *>(
+                a.lg + ((size_t)unit * G + hk) * a.lg_stride + t0 + tt + 4 * qd) = lg;
+    };
+    // One key batch.  The next batch's words of tile j are requested into
+    // tile j's registers as soon as its MFMAs have read them, so each tile's
+    // words have one batch of work to arrive.
     for (int b = 0; b < nbatch; ++b) {
         const int tok = b * BT;                   // wave-relative
         const int nxt = min(tok + BT, last);      // next batch (clamped)
         if constexpr (G > 1) {
-            if (tok % bblk == 0) {                // a new key operand
+            if ((tok & (bblk - 1)) == 0) {        // a new key operand
                 build_b();
                 build_bias();
                 wave_lds_sync();
@@ -457,72 +557,63 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        const int gb = (tok / bblk) * NG;         // first group of the operand
+        const int gb = (tok >> bb_sh) << NG_SH;   // first group of the operand
 #pragma unroll
         for (int j = 0; j < TPB; ++j) {
             // tiles past the end use clamped rows and are never read
             const int tl = min(tok + 16 * j, nt - 16);
             float4_t acc = {0.f, 0.f, 0.f, 0.f};
+            half8_t av[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) av[kb] = key_operand(kw, j, kb, 0);
+            if constexpr (!ONE && KP < 4) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_ktile(nxt, j, kw);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const half8_t av = key_operand(j, kb, 0);
-                acc = mfma16(av, bhi[kb], acc);
-                acc = mfma16(av, blo[kb], acc);
+                acc = mfma16(av[kb], bhi[kb], acc);
+                acc = mfma16(av[kb], blo[kb], acc);
             }
             if constexpr (KP == 4) {              // the high 4 bits of 8-bit codes
                 float4_t acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
-                    const half8_t av = key_operand(j, kb, 2);
-                    acc2 = mfma16(av, bhi[kb], acc2);
-                    acc2 = mfma16(av, blo[kb], acc2);
+                    const half8_t av2 = key_operand(kw, j, kb, 2);
+                    acc2 = mfma16(av2, bhi[kb], acc2);
+                    acc2 = mfma16(av2, blo[kb], acc2);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(acc2[i], 16.f, acc[i]);
             }
-            if (per_lane) {
-                if (tok + 16 * j < nt && gcol == tl / Gk - gb) keep = acc;
-            } else if (gcol == tl / Gk - gb && tok + 16 * j < nt) {
-                const float bz = L.bias[(tl / Gk - gb) * G + hk];
-                float4_t lg;
+            const int grp = (tl >> gk_sh) - gb;   // the tile's column group
+            if (per_lane) {                       // a select, not a branch
+                const bool take = tok + 16 * j < nt && gcol == grp;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    lg[i] = __builtin_fmaf(acc[i], kfac, bz);
-                    mloc = fmaxf(mloc, lg[i]);
-                }
-                *reinterpret_cast<float4_t *>(&L.ls[hk * kLsStride + tok + 16 * j + 4 * qd]) = lg;
-                if constexpr (MASS)               // the mass audit's logits
-                    *reinterpret_cast<float4_t *>(
-                        a.lg + ((size_t)unit * G + hk) * a.lg_stride + t0 + tok + 16 * j +
-                        4 * qd) = lg;
+                for (int i = 0; i < 4; ++i) keep[i] = take ? acc[i] : keep[i];
+            } else if (gcol == grp && tok + 16 * j < nt) {
+                store_logits(acc, L.bias[grp * G + hk], tok + 16 * j);
             }
         }
-        if constexpr (!ONE) {
+        // the operand's last batch: the kept tiles' logits
+        if (per_lane && (((tok + BT) & (bblk - 1)) == 0 || tok + BT >= nt)) {
+            const int tt = (tok & ~(bblk - 1)) + 16 * gcol;
+            if (tt < nt) store_logits(keep, L.bias[gcol * G + hk], tt);
+        }
+        if constexpr (!ONE && KP == 4) {          // four planes: all at the end
             __builtin_amdgcn_sched_barrier(0);
-            load_kwords(nxt);
+            load_kwords(nxt, kw);
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
-    if (per_lane && 16 * gcol < nt) {             // this lane's tile: gcol
-        const float bz = L.bias[gcol * G + hk];
-        float4_t lg;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            lg[i] = __builtin_fmaf(keep[i], kfac, bz);
-            mloc = fmaxf(mloc, lg[i]);
-        }
-        *reinterpret_cast<float4_t *>(&L.ls[hk * kLsStride + 16 * gcol + 4 * qd]) = lg;
-        if constexpr (MASS)
-            *reinterpret_cast<float4_t *>(
-                a.lg + ((size_t)unit * G + hk) * a.lg_stride + t0 + 16 * gcol + 4 * qd) = lg;
     }
 
     // ================================================== softmax, staging
-    for (int off = G; off < 64; off <<= 1) mloc = fmaxf(mloc, shfl_xor(mloc, off));
+    mloc = strided_max<G>(mloc);                  // lane l: head l % G
     float m_h[G], l_h[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        m_h[h] = __shfl(mloc, h, 64);
+        m_h[h] = __builtin_amdgcn_readlane(mloc, h);
         l_h[h] = 0.f;
     }
     wave_lds_sync();
@@ -577,15 +668,37 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     }
     const int nsteps = nt32 >> 5;
     // one 32-token step of every pass; `code(P, mb)` gives the step's value
-    // word, `after(P)` runs once the pass's words are in code operands
-    auto step = [&](int e, auto &&code, auto &&after) {
-        const int st = 32 * e;
+    // word, `after(P)` runs once the pass's words are in code operands.  A
+    // step with `live` false (the padding step of an odd count) re-reads
+    // the last step's LDS rows and multiplies with zero probabilities, so
+    // it adds exactly nothing; the step pair then has no branch, and the
+    // loads two steps ahead keep their place in the wait counts.
+    auto step = [&](int e, bool live, auto &&code, auto &&after) {
+        const int st = 32 * min(e, nsteps - 1);
         const float *pp = &L.ls[hc * kLsStride + st + tb];
-        const float4_t p0 = *reinterpret_cast<const float4_t *>(pp);
-        const float4_t p1 = *reinterpret_cast<const float4_t *>(pp + 8);
+        float4_t p0 = *reinterpret_cast<const float4_t *>(pp);
+        float4_t p1 = *reinterpret_cast<const float4_t *>(pp + 8);
+        // several passes: every pass's scale and zero reads up front, so the
+        // step waits for LDS once
+        half4_t s0h[NPASS], s1h[NPASS], z0h[NPASS], z1h[NPASS];
+        auto read_meta = [&](int P) {
+            const int vg = P * GPP + r % GPP;
+            const half_t *sp = &L.sv[vg * kSvStride + st + tb];
+            const half_t *zp = &L.zv[vg * kSvStride + st + tb];
+            s0h[P] = *reinterpret_cast<const half4_t *>(sp);
+            s1h[P] = *reinterpret_cast<const half4_t *>(sp + 8);
+            z0h[P] = *reinterpret_cast<const half4_t *>(zp);
+            z1h[P] = *reinterpret_cast<const half4_t *>(zp + 8);
+        };
+        if constexpr (NPASS > 1)
+#pragma unroll
+            for (int P = 0; P < NPASS; ++P) read_meta(P);
+        if (!live) {
+            p0 = float4_t{0.f, 0.f, 0.f, 0.f};
+            p1 = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int P = 0; P < NPASS; ++P) {
-            const int vg = P * GPP + r % GPP;
             half8_t av[MBP];
 #pragma unroll
             for (int mb = 0; mb < MBP; ++mb) {
@@ -596,12 +709,8 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                                            code(P, MBP + mb) >> (8 * (qd & 1)));
             }
             after(P);
-            const half_t *sp = &L.sv[vg * kSvStride + st + tb];
-            const half_t *zp = &L.zv[vg * kSvStride + st + tb];
-            const half4_t s0 = *reinterpret_cast<const half4_t *>(sp);
-            const half4_t s1 = *reinterpret_cast<const half4_t *>(sp + 8);
-            const half4_t z0 = *reinterpret_cast<const half4_t *>(zp);
-            const half4_t z1 = *reinterpret_cast<const half4_t *>(zp + 8);
+            if constexpr (NPASS == 1) read_meta(P);
+            const half4_t s0 = s0h[P], s1 = s1h[P], z0 = z0h[P], z1 = z1h[P];
             u32x4 bhw, blw;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -627,7 +736,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
 #pragma unroll
         for (int e = 0; e < NVE; ++e) {
             if (e >= nsteps) break;               // uniform
-            step(e, [&](int P, int mb) { return vwe[P][e][mb]; }, [](int) {});
+            step(e, true, [&](int P, int mb) { return vwe[P][e][mb]; }, [](int) {});
         }
     } else {
         // value words two steps ahead: buffer A holds even steps, B odd
@@ -636,18 +745,27 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         for (int P = 0; P < NPASS; ++P) load_vw(P, 0, vwA[P]);
 #pragma unroll
         for (int P = 0; P < NPASS; ++P) load_vw(P, min(32, nt32 - 32), vwB[P]);
-        for (int e = 0; e < nsteps; e += 2) {
-            step(e, [&](int P, int mb) { return vwA[P][mb]; }, [&](int P) {
+        auto pair = [&](int e) {
+            step(e, true, [&](int P, int mb) { return vwA[P][mb]; }, [&](int P) {
                 __builtin_amdgcn_sched_barrier(0);
                 load_vw(P, min(32 * (e + 2), nt32 - 32), vwA[P]);
                 __builtin_amdgcn_sched_barrier(0);
             });
-            if (e + 1 < nsteps)                   // uniform
-                step(e + 1, [&](int P, int mb) { return vwB[P][mb]; }, [&](int P) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_vw(P, min(32 * (e + 3), nt32 - 32), vwB[P]);
-                    __builtin_amdgcn_sched_barrier(0);
-                });
+            step(e + 1, e + 1 < nsteps, [&](int P, int mb) { return vwB[P][mb]; }, [&](int P) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_vw(P, min(32 * (e + 3), nt32 - 32), vwB[P]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        if (NPASS > 1 && nsteps == kMaxWaveChunk / 32) {
+            // a full wave share: straight-line steps, so each wait for the
+            // value words leaves the next step's loads in flight (in the
+            // loop the compiler waits for all of them); one pass (g = 1)
+            // keeps the loop, whose registers then fit four waves per SIMD
+#pragma unroll
+            for (int e = 0; e < kMaxWaveChunk / 32; e += 2) pair(e);
+        } else {
+            for (int e = 0; e < nsteps; e += 2) pair(e);
         }
     }
     float zsum[NPASS];
@@ -655,8 +773,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     for (int P = 0; P < NPASS; ++P) {
         float zt = za[P][0] + __builtin_amdgcn_ldexpf(za[P][1], 2) +
                    __builtin_amdgcn_ldexpf(za[P][2], 4) + __builtin_amdgcn_ldexpf(za[P][3], 6);
-        zt += shfl_xor(zt, 16);
-        zt += shfl_xor(zt, 32);
+        zt = xor32_sum(xor16_sum(zt));
         zsum[P] = zt;
     }
     wave_lds_sync();
@@ -756,8 +873,7 @@ __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         float m = mloc[h];
-        m = fmaxf(m, shfl_xor(m, 16));
-        m = fmaxf(m, shfl_xor(m, 32));
+        m = xor32_max(xor16_max(m));
         m_h[h] = m;
         l_h[h] = 0.f;
     }
@@ -801,8 +917,7 @@ __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             float v = o[h][i];
-            v += shfl_xor(v, 16);
-            v += shfl_xor(v, 32);
+            v = xor32_sum(xor16_sum(v));
             o[h][i] = v;
         }
     wave_lds_sync();
@@ -824,7 +939,7 @@ __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0
 // KP, VP: 2-bit planes of the key / value codes (packed_wave).
 template <int D, int G, bool FULLV, bool ONE, bool MASS, int W = kWaves, int KP = 1,
           int VP = 1>
-__global__ __launch_bounds__(W * 64, (G == 2 || G == 8 || KP == 4) ? 2 : 3) void decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(W * 64, (G == 2 || G == 8 || KP == 4) ? 2 : (G == 1 && !ONE && KP == 1 && VP == 1) ? 4 : 3) void decode_kernel(DecArgs a) {
     // x = unit, y = split: with the round-robin dispatch of workgroups over
     // the 8 XCDs, every split of a unit (and its merge below) runs on the
     // XCD unit mod 8 when the unit count is a multiple of 8.
@@ -1337,7 +1452,7 @@ hipError_t launch_decode_segs(const uint16_t *q, uint16_t *o, int units, int g,
         a.n_res = s == n_seg - 1 ? n_res : 0;
         a.chunk = p.chunk;
         a.waves = p.waves;
-        a.n_chunks = p.n_chunks;
+            a.n_chunks = p.n_chunks;
         a.nsplit = p.nsplit;
         a.res_split = p.res_split;
         a.res_wave0 = p.res_wave0;
