@@ -52,7 +52,7 @@ def parse():
                    help="workload id (configs.py); default: the 131072-token "
                         "Llama-3-8B-shaped GQA stack, the largest that fits "
                         "one GPU")
-    p.add_argument("--sub-configs", default="3,4",
+    p.add_argument("--sub-configs", default="3,4,2",
                    help="comma-separated workloads measured after the "
                         "headline one, one sub-record each ('' for none)")
     p.add_argument("--sub-steps", type=int, default=1)
@@ -505,11 +505,18 @@ def run_workload(cfg_id, steps, warmup, args, stream, headline):
             "frac": round(pre_achieved / MFMA_FP16_PEAK_TFLOPS, 4),
             "avg_launch_us": round(float(pre_call_ms.mean()) * 1e3, 3),
             "algorithmic_flops_per_launch": prefill_flops(c),
+            # context only: the FlashAttention convention counts pass 1's
+            # 2 D n (n+1) per query head and not the score pass
+            "achieved_pass1_convention": round(pre_achieved * 2 / 3, 2),
         },
         "input_generation_s": round(gen_s, 1),
     }
     if mass_rec:
         rec["decode_mass_audit"] = mass_rec
+    if avg_dec_bytes < 64e6 and dec_call_ms * 1e3 < 20:
+        rec["roofline"]["regime"] = ("launch-bound: about %.0f MB per call, "
+                                     "timed as a graph of every layer's call"
+                                     % (avg_dec_bytes / 1e6))
     state = dict(c=c, ks=ks, r=r, dims=dims, qkv=qkv, dq=dq, dk=dk, dv=dv)
     del graphs, caches, cols, sels, out, ws_pref, ws_dec
     return rec, state
