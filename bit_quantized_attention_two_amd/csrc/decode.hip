@@ -1122,10 +1122,12 @@ __global__ __launch_bounds__(kThreads) void decode_mass_kernel(
 // Largest chunk whose blocks still fill half of the resident block slots
 // (blocks per CU from the kernels' register and LDS use: 4 for g = 1, 3
 // for g = 4, 2 for g = 2 and 8), never more than kMaxSplit - 1 packed
-// splits per unit.  A wave's share is a power of two between
+// splits per unit.  A 4-wave block's wave share is a power of two between
 // max(kMinWaveChunk, Gk) and kMaxWaveChunk tokens, so it holds whole key
-// groups and whole 32-token value steps.
-int pick_chunk(int units, int n_packed, int Gk, int g, bool mass) {
+// groups and whole 32-token value steps; a 12-wave block's is a multiple of
+// the key group (and of 16) up to kMaxWaveChunk, its last value step
+// possibly partial.
+int pick_chunk(int units, int n_packed, int n_res, int Gk, int g, bool mass) {
     const int per_cu = g == 1 ? 4 : g == 4 ? 3 : 2;
     const long want = 256L * per_cu / 2;
     const int minw = std::max(kMinWaveChunk, Gk);
@@ -1140,17 +1142,49 @@ int pick_chunk(int units, int n_packed, int Gk, int g, bool mass) {
         }
     }
     // g = 4: one 12-wave block per CU when such a grid fills the chip in one
-    // round (240-256 blocks), or fills at least 3/4 of it while the 4-wave
-    // form would need splits of 512 tokens or fewer.  Three 4-wave blocks per
-    // CU all start together, and the instruction arbiter's preference for
-    // older waves then makes the third block of each CU finish ~35% after
-    // the first, so the call ends with the CUs a third occupied; the waves of
-    // one block share one age and finish together.
-    if (g == 4 && !mass) {
+    // round.  Three 4-wave blocks per CU all start together, and the
+    // instruction arbiter's preference for older waves then makes the third
+    // block of each CU finish ~35% after the first, so the call ends with
+    // the CUs a third occupied; the waves of one block share one age.  The
+    // call's time follows the tokens per CU, and longer wave shares cost less
+    // per token, so:
+    // - a power-of-two share whose grid fills 240-256 CUs (or 192 while the
+    //   4-wave form would need splits of 512 tokens or fewer);
+    // - else, when the 4-wave grid would give some CUs a third block, the
+    //   finest share (a multiple of the key group and of 16) whose grid fits
+    //   one round and fills at least 224 CUs;
+    // - else the 4-wave form (at most two blocks per CU).
+    // A residual that finds no idle waves in the last split adds a split per
+    // unit, so it counts in the grid.
+    if (g == 4 && !mass && units <= 256) {
+        auto blocks12 = [&](long w) {
+            const long ch = kBigWaves * w;
+            const long sp = (n_packed + ch - 1) / ch;
+            long extra = 0;
+            if (n_res > 0) {
+                const long used = sp > 0 ? (n_packed - (sp - 1) * ch + w - 1) / w : kBigWaves;
+                if (kBigWaves - used < (n_res + 63) / 64) extra = 1;
+            }
+            return (long)units * (sp + extra);
+        };
         for (int w = kMaxWaveChunk; w >= minw; w >>= 1) {
-            const long big = (long)units * ((n_packed + kBigWaves * w - 1) / (kBigWaves * w));
+            const long big = blocks12(w);
             if (big <= 256 && (big >= 240 || (big >= 192 && ch4 <= 512)))
                 return kBigWaves * w;
+        }
+        const long b4 = (long)units * ((n_packed + ch4 - 1) / ch4);
+        if (b4 > 512) {
+            const int step = std::max(16, Gk);
+            const long per_unit = 256 / units;        // blocks per unit, one round
+            long w = (n_packed + kBigWaves * per_unit - 1) / (kBigWaves * per_unit);
+            w = std::max<long>((w + step - 1) / step * step, minw);
+            for (; w <= kMaxWaveChunk; w += step) {
+                const long big = blocks12(w);
+                if (big <= 256) {
+                    if (big >= 224) return (int)(kBigWaves * w);
+                    break;
+                }
+            }
         }
     }
     return ch4;
@@ -1321,7 +1355,7 @@ struct Plan {
 // segments have no 12-wave form).
 static Plan make_plan(int units, int g, int n_packed, int n_res, int Gk, bool no_big) {
     Plan p;
-    p.chunk = pick_chunk(units, n_packed, Gk, g, no_big);
+    p.chunk = pick_chunk(units, n_packed, n_res, Gk, g, no_big);
     p.waves = p.chunk % kBigWaves == 0 ? kBigWaves : kWaves;   // W = 4 chunks are 2^k
     p.n_chunks = (n_packed + p.chunk - 1) / p.chunk;
     p.nsplit = p.n_chunks;

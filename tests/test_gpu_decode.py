@@ -206,13 +206,15 @@ def test_decode_multi_batch_waves(D, g, Gv):
 
 @pytest.mark.parametrize("n,m,D,Gk,Gv", [
     (41000, 40000, 128, 16, 16), (24000, 23400, 128, 16, 16),
+    (81000, 80000, 128, 16, 16), (71000, 70000, 128, 16, 16),
     (41000, 40000, 64, 16, 16), (41000, 40000, 128, 64, 32)])
 def test_decode_one_round_gqa(n, m, D, Gk, Gv):
-    """g = 4 calls in the one-round 12-wave form: 8 kv heads x 27 splits of
-    1536 tokens (128 per wave; the 4-wave form would need 512-token splits)
-    and 8 kv heads x 31 splits of 768 tokens (64 per wave), at D = 128 and
-    64, and with key groups of 64 tokens and value groups of 32 channels;
-    every unit against the oracle."""
+    """g = 4 calls in the one-round 12-wave form, 8 kv heads: 27 splits of
+    128-token wave shares (the 4-wave form would need 512-token splits), 31
+    of 64, and, where the 4-wave grid would give some CUs a third block,
+    30 splits of 224 (seven 32-token value steps, an odd count) and 31 of
+    192; at D = 128 and 64, and with key groups of 64 tokens and value
+    groups of 32 channels; every unit against the oracle."""
     torch, mk = require_gpu()
     B, Hkv, g = 1, 8, 4
     say("decode-one-round-gqa", dict(n=n, m=m, D=D, Gk=Gk, Gv=Gv))
