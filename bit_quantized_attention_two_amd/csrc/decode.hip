@@ -49,6 +49,7 @@
 // it there for later calls.
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -300,44 +301,19 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     const int hk = r % G;
     const int gcol = r / G;
 
-    // ---- this lane's q channels as fp16 pairs (hf = 0, 1) per (kb, i), in
-    // the k-slot order of the key operands; the power of two 2^e > max |q_h|
-    // per head; then q 2^(-e-2i) in place.
-    uint32_t qh[KB][4];
-    float qmax = 0.f;
+    // ---- this lane's q channels, k-block kb, halves hf = 0, 1 (requested
+    // here, used after the first key loads are issued)
+    uint2 qx[KB][2];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         const int w = (qd >> 1) * KB + kb;
-        const uint2 x0 = *reinterpret_cast<const uint2 *>(
-            qu + (size_t)hk * D + 16 * w + 4 * (qd & 1));
-        const uint2 x1 = *reinterpret_cast<const uint2 *>(
-            qu + (size_t)hk * D + 16 * w + 4 * (qd & 1) + 8);
-        const uint32_t a0[2] = {x0.x, x0.y}, a1[2] = {x1.x, x1.y};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = (a0[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-            const uint32_t hi = (a1[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-            qh[kb][i] = lo | (hi << 16);
-            qmax = fmaxf(qmax, fmaxf(fabsf(h2f((uint16_t)lo)), fabsf(h2f((uint16_t)hi))));
-        }
+        for (int hf = 0; hf < 2; ++hf)
+            qx[kb][hf] = *reinterpret_cast<const uint2 *>(
+                qu + (size_t)hk * D + 16 * w + 4 * (qd & 1) + 8 * hf);
     }
-    qmax = xor32_max(xor16_max(qmax));
-    // any e with 2^e > max |q| keeps |q 2^-e| < 1; e >= -8 keeps the factors
-    // 2^(-e-2i) within fp16
-    const int qe = max(__builtin_amdgcn_frexp_expf(qmax), -8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const half_t f = (half_t)__builtin_amdgcn_ldexpf(1.f, -qe - 2 * i);   // exact
-        const half2_t ff = {f, f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-            qh[kb][i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, qh[kb][i]) * ff);
-    }
-    // logit (log2 units) = (acc * 2^(24 + e) + z term) * qscale
-    const float kfac = __builtin_amdgcn_ldexpf(a.qscale, 24 + qe);
-    // the z terms' MFMA takes z 4^(i-3) against q 2^(-e-2i)
-    const float zfac = __builtin_amdgcn_ldexpf(a.qscale, 6 + qe);
-
+    uint32_t qh[KB][4];                           // q 2^(-e-2i), set below
+    float kfac, zfac;                             // logit and z-term factors
 
     // ---- loaders (indices clamped, never predicated)
     uint2 ksr[KB][2];                             // key scales of a B operand
@@ -352,9 +328,12 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                     ks + (size_t)gs * D + 16 * w + 4 * (qd & 1) + 8 * hf);
         }
     };
-    uint2 kzr[KB][2];                             // key zeros, rows = groups
+    // key zeros, rows = the 16 groups of the window [16 m, 16 m + 16) of
+    // wave-relative groups that holds tok's group (a window spans 16 / NG key
+    // operands, so its z terms are computed once for all of them)
+    uint2 kzr[KB][2];
     auto load_kzero = [&](int tok) {
-        const int gz = g_first + min(((tok >> bb_sh) << NG_SH) + r, n_grp - 1);
+        const int gz = g_first + min(((tok >> gk_sh) & ~15) + r, n_grp - 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int w = (qd >> 1) * KB + kb;
@@ -498,6 +477,8 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     };
 
     // ============================================================ phase K
+    // the first batch's key loads go out with q's, so they share its trip
+    __builtin_amdgcn_sched_barrier(0);
     load_kscale(0);
     load_kzero(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -514,6 +495,39 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             for (int e = 0; e < NVE; ++e) load_vw(P, 32 * e, vwe[P][e]);
         __builtin_amdgcn_sched_barrier(0);
     }
+
+    // ---- q as fp16 pairs (hf = 0, 1) per (kb, i), in the k-slot order of
+    // the key operands; the power of two 2^e > max |q_h| per head; then
+    // q 2^(-e-2i) in place.
+    float qmax = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const uint32_t a0[2] = {qx[kb][0].x, qx[kb][0].y}, a1[2] = {qx[kb][1].x, qx[kb][1].y};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = (a0[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+            const uint32_t hi = (a1[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+            qh[kb][i] = lo | (hi << 16);
+            qmax = fmaxf(qmax, fmaxf(fabsf(h2f((uint16_t)lo)), fabsf(h2f((uint16_t)hi))));
+        }
+    }
+    qmax = xor32_max(xor16_max(qmax));
+    // any e with 2^e > max |q| keeps |q 2^-e| < 1; e >= -8 keeps the factors
+    // 2^(-e-2i) within fp16
+    const int qe = max(__builtin_amdgcn_frexp_expf(qmax), -8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const half_t f = (half_t)__builtin_amdgcn_ldexpf(1.f, -qe - 2 * i);   // exact
+        const half2_t ff = {f, f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            qh[kb][i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, qh[kb][i]) * ff);
+    }
+    // logit (log2 units) = (acc * 2^(24 + e) + z term) * qscale
+    kfac = __builtin_amdgcn_ldexpf(a.qscale, 24 + qe);
+    // the z terms' MFMA takes z 4^(i-3) against q 2^(-e-2i)
+    zfac = __builtin_amdgcn_ldexpf(a.qscale, 6 + qe);
+
     if constexpr (G == 1) {                       // 16 groups cover the wave
         build_b();
         build_bias();
@@ -538,26 +552,47 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             *reinterpret_cast<float4_t *>(
                 a.lg + ((size_t)unit * G + hk) * a.lg_stride + t0 + tt + 4 * qd) = lg;
     };
+    // PF (GQA, several batches): the last key batch requests the value meta
+    // and the first two value steps where the other batches request the next
+    // batch's keys, so phase V's first loads overlap the last logits (these
+    // kernels have the registers to spare at their occupancy).
+    constexpr bool PF = G > 1 && !ONE && KP < 4;
+    const int nt32 = (nt + 31) & ~31;
+    uint32_t vwA[NPASS][MBP * VP], vwB[NPASS][MBP * VP];   // value words, even / odd steps
+    auto load_v_first = [&]() {
+#pragma unroll
+        for (int k = 0; k < NK; ++k) load_vmeta(k);
+#pragma unroll
+        for (int P = 0; P < NPASS; ++P) load_vw(P, 0, vwA[P]);
+#pragma unroll
+        for (int P = 0; P < NPASS; ++P) load_vw(P, min(32, nt32 - 32), vwB[P]);
+    };
     // One key batch.  The next batch's words of tile j are requested into
     // tile j's registers as soon as its MFMAs have read them, so each tile's
     // words have one batch of work to arrive.
-    for (int b = 0; b < nbatch; ++b) {
+    auto kbatch = [&](int b, auto lastb) {
+        constexpr bool LASTB = decltype(lastb)::value;
         const int tok = b * BT;                   // wave-relative
         const int nxt = min(tok + BT, last);      // next batch (clamped)
+        const int gb = (tok >> bb_sh) << NG_SH;   // first group of the operand
+        const int gw = gb & 15;                   // its row in the z-term window
         if constexpr (G > 1) {
             if ((tok & (bblk - 1)) == 0) {        // a new key operand
                 build_b();
-                build_bias();
+                if (gw == 0) build_bias();        // a new window
                 wave_lds_sync();
             }
             if constexpr (!ONE) {
                 __builtin_amdgcn_sched_barrier(0);
-                load_kscale(nxt);
-                load_kzero(nxt);
+                if constexpr (LASTB) {
+                    load_v_first();
+                } else {
+                    load_kscale(nxt);
+                    if (((nxt >> gk_sh) ^ (tok >> gk_sh)) & ~15) load_kzero(nxt);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        const int gb = (tok >> bb_sh) << NG_SH;   // first group of the operand
 #pragma unroll
         for (int j = 0; j < TPB; ++j) {
             // tiles past the end use clamped rows and are never read
@@ -566,7 +601,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             half8_t av[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) av[kb] = key_operand(kw, j, kb, 0);
-            if constexpr (!ONE && KP < 4) {
+            if constexpr (!ONE && KP < 4 && !LASTB) {
                 __builtin_amdgcn_sched_barrier(0);
                 load_ktile(nxt, j, kw);
                 __builtin_amdgcn_sched_barrier(0);
@@ -593,19 +628,25 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) keep[i] = take ? acc[i] : keep[i];
             } else if (gcol == grp && tok + 16 * j < nt) {
-                store_logits(acc, L.bias[grp * G + hk], tok + 16 * j);
+                store_logits(acc, L.bias[(gw + grp) * G + hk], tok + 16 * j);
             }
         }
         // the operand's last batch: the kept tiles' logits
         if (per_lane && (((tok + BT) & (bblk - 1)) == 0 || tok + BT >= nt)) {
             const int tt = (tok & ~(bblk - 1)) + 16 * gcol;
-            if (tt < nt) store_logits(keep, L.bias[gcol * G + hk], tt);
+            if (tt < nt) store_logits(keep, L.bias[(gw + gcol) * G + hk], tt);
         }
         if constexpr (!ONE && KP == 4) {          // four planes: all at the end
             __builtin_amdgcn_sched_barrier(0);
             load_kwords(nxt, kw);
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    if constexpr (PF) {
+        for (int b = 0; b + 1 < nbatch; ++b) kbatch(b, std::false_type{});
+        kbatch(nbatch - 1, std::true_type{});
+    } else {
+        for (int b = 0; b < nbatch; ++b) kbatch(b, std::false_type{});
     }
 
     // ================================================== softmax, staging
@@ -617,10 +658,9 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         l_h[h] = 0.f;
     }
     wave_lds_sync();
-    const int nt32 = (nt + 31) & ~31;
     // the value meta of all of this lane's tokens (t = lane + 64 k), loads
     // issued together so that their latencies overlap
-    if constexpr (!ONE)
+    if constexpr (!ONE && !PF)
 #pragma unroll
         for (int k = 0; k < NK; ++k) load_vmeta(k);
 #pragma unroll
@@ -740,11 +780,12 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         }
     } else {
         // value words two steps ahead: buffer A holds even steps, B odd
-        uint32_t vwA[NPASS][MBP * VP], vwB[NPASS][MBP * VP];
+        if constexpr (!PF) {
 #pragma unroll
-        for (int P = 0; P < NPASS; ++P) load_vw(P, 0, vwA[P]);
+            for (int P = 0; P < NPASS; ++P) load_vw(P, 0, vwA[P]);
 #pragma unroll
-        for (int P = 0; P < NPASS; ++P) load_vw(P, min(32, nt32 - 32), vwB[P]);
+            for (int P = 0; P < NPASS; ++P) load_vw(P, min(32, nt32 - 32), vwB[P]);
+        }
         auto pair = [&](int e) {
             step(e, true, [&](int P, int mb) { return vwA[P][mb]; }, [&](int P) {
                 __builtin_amdgcn_sched_barrier(0);
