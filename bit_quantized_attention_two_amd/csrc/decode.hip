@@ -786,13 +786,13 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
 #pragma unroll
             for (int P = 0; P < NPASS; ++P) load_vw(P, min(32, nt32 - 32), vwB[P]);
         }
-        auto pair = [&](int e) {
+        auto pair = [&](int e, bool full) {
             step(e, true, [&](int P, int mb) { return vwA[P][mb]; }, [&](int P) {
                 __builtin_amdgcn_sched_barrier(0);
                 load_vw(P, min(32 * (e + 2), nt32 - 32), vwA[P]);
                 __builtin_amdgcn_sched_barrier(0);
             });
-            step(e + 1, e + 1 < nsteps, [&](int P, int mb) { return vwB[P][mb]; }, [&](int P) {
+            step(e + 1, full || e + 1 < nsteps, [&](int P, int mb) { return vwB[P][mb]; }, [&](int P) {
                 __builtin_amdgcn_sched_barrier(0);
                 load_vw(P, min(32 * (e + 3), nt32 - 32), vwB[P]);
                 __builtin_amdgcn_sched_barrier(0);
@@ -804,9 +804,9 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             // loop the compiler waits for all of them); one pass (g = 1)
             // keeps the loop, whose registers then fit four waves per SIMD
 #pragma unroll
-            for (int e = 0; e < kMaxWaveChunk / 32; e += 2) pair(e);
+            for (int e = 0; e < kMaxWaveChunk / 32; e += 2) pair(e, true);
         } else {
-            for (int e = 0; e < nsteps; e += 2) pair(e);
+            for (int e = 0; e < nsteps; e += 2) pair(e, false);
         }
     }
     float zsum[NPASS];
@@ -993,7 +993,6 @@ __global__ __launch_bounds__(W * 64, (G == 2 || G == 8 || KP == 4) ? 2 : (G == 1
 
     __shared__ WaveLds<D, G> lds[W];
     __shared__ float red_ml[W][G][2];
-    __shared__ float mrg[G][2];
 
     float m_w[G], l_w[G];
 #pragma unroll
@@ -1038,32 +1037,38 @@ __global__ __launch_bounds__(W * 64, (G == 2 || G == 8 || KP == 4) ? 2 : (G == 1
         }
     __syncthreads();
 
-    // ----------------------------------------- merge the 4 waves, store
-    if (tid < G) {
-        float M = -INFINITY;
-        for (int w = 0; w < W; ++w)
-            if (red_ml[w][tid][1] > 0.f) M = fmaxf(M, red_ml[w][tid][0]);
-        float L = 0.f;
-        for (int w = 0; w < W; ++w)
-            if (red_ml[w][tid][1] > 0.f)
-                L += red_ml[w][tid][1] * __builtin_amdgcn_exp2f(red_ml[w][tid][0] - M);
-        mrg[tid][0] = M;
-        mrg[tid][1] = L;
-    }
-    __syncthreads();
+    // ----------------------------------------- merge the waves, store
+    // Every thread reads its head's (max, sum) of all W waves at once (LDS
+    // broadcasts, one wait) and takes them with selects, not branches: a
+    // chain of dependent LDS reads here would add microseconds to every
+    // block's tail.
     const size_t sbase = (size_t)unit * a.nsplit_total + a.split_off + split;
     for (int i = tid; i < G * D; i += (W * 64)) {
         const int h = i / D;
-        const float M = mrg[h][0];
-        float v = 0.f;
-        for (int w = 0; w < W; ++w)
-            if (red_ml[w][h][1] > 0.f)
-                v += lds[w].ls[i] * __builtin_amdgcn_exp2f(red_ml[w][h][0] - M);
+        float mw[W], lw[W], ow[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            mw[w] = red_ml[w][h][0];
+            lw[w] = red_ml[w][h][1];
+            ow[w] = lds[w].ls[i];
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) M = lw[w] > 0.f ? fmaxf(M, mw[w]) : M;
+        float v = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            // a wave without tokens wrote no output: its LDS is not read
+            const bool ok = lw[w] > 0.f;
+            const float e = ok ? __builtin_amdgcn_exp2f(mw[w] - M) : 0.f;
+            v = __builtin_fmaf(ok ? ow[w] : 0.f, e, v);
+            L = __builtin_fmaf(lw[w], e, L);
+        }
         a.part_o[sbase * G * D + i] = v;
-    }
-    if (tid < G) {
-        a.part_ml[(sbase * G + tid) * 2 + 0] = mrg[tid][0];
-        a.part_ml[(sbase * G + tid) * 2 + 1] = mrg[tid][1];
+        if (i % D == 0) {
+            a.part_ml[(sbase * G + h) * 2 + 0] = M;
+            a.part_ml[(sbase * G + h) * 2 + 1] = L;
+        }
     }
 }
 
@@ -1087,33 +1092,48 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     const float *ml = part_ml + (size_t)unit * nsplit * G * 2 + h * 2;
     const float *po = part_o + (size_t)unit * nsplit * G * D + h * D + ch;
 
+    constexpr int STEP = NB * SLICES;
     float m_run = -INFINITY, l_run = 0.f, o_run = 0.f;
-    for (int s0 = slice; s0 < nsplit; s0 += NB * SLICES) {
-        float mb[NB], lb[NB], ob[NB];
+    typedef float Batch[3][NB];                   // (max, sum, o) of NB splits
+    auto load = [&](int s0, Batch &b) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int s = min(s0 + i * SLICES, nsplit - 1);
-            mb[i] = ml[(size_t)s * G * 2];
-            lb[i] = ml[(size_t)s * G * 2 + 1];
-            ob[i] = po[(size_t)s * G * D];
+            b[0][i] = ml[(size_t)s * G * 2];
+            b[1][i] = ml[(size_t)s * G * 2 + 1];
+            b[2][i] = po[(size_t)s * G * D];
         }
+    };
+    // selects, not branches, so that the o loads are not held back behind
+    // the (max, sum) ones
+    auto fold = [&](int s0, const Batch &b) {
         float mx = m_run;
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            if (s0 + i * SLICES < nsplit && lb[i] > 0.f) mx = fmaxf(mx, mb[i]);
-        if (mx == -INFINITY) continue;
-        const float sc = __builtin_amdgcn_exp2f(m_run - mx);
+            mx = (s0 + i * SLICES < nsplit && b[1][i] > 0.f) ? fmaxf(mx, b[0][i]) : mx;
+        const float sc = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
         l_run *= sc;
         o_run *= sc;
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            if (s0 + i * SLICES < nsplit && lb[i] > 0.f) {
-                const float w = __builtin_amdgcn_exp2f(mb[i] - mx);
-                l_run += lb[i] * w;
-                o_run += ob[i] * w;
-            }
+            const bool ok = s0 + i * SLICES < nsplit && b[1][i] > 0.f;
+            const float w = ok ? __builtin_amdgcn_exp2f(b[0][i] - mx) : 0.f;
+            l_run = __builtin_fmaf(ok ? b[1][i] : 0.f, w, l_run);
+            o_run = __builtin_fmaf(ok ? b[2][i] : 0.f, w, o_run);
         }
         m_run = mx;
+    };
+    // the first two batches are requested together (up to 2 STEP splits in
+    // one round trip), any further ones a batch at a time
+    Batch b0, b1;
+    load(slice, b0);
+    const bool two = nsplit > STEP;               // uniform
+    if (two) load(slice + STEP, b1);
+    fold(slice, b0);
+    if (two) fold(slice + STEP, b1);
+    for (int s0 = slice + 2 * STEP; s0 < nsplit; s0 += STEP) {
+        load(s0, b0);
+        fold(s0, b0);
     }
     r_m[tid] = m_run;
     r_l[tid] = l_run;
