@@ -317,16 +317,18 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
 
     // ---- loaders (indices clamped, never predicated)
     uint2 ksr[KB][2];                             // key scales of a B operand
+    // the lane's channels within a scale row, in bytes
+    const uint32_t ks_lane = (uint32_t)(16 * (qd >> 1) * KB + 4 * (qd & 1)) * 2u;
     auto load_kscale = [&](int tok) {             // B operand holding tok
-        const int gs = g_first + min(((tok >> bb_sh) << NG_SH) + gcol, n_grp - 1);
+        const int gb = (tok >> bb_sh) << NG_SH;   // uniform
+        // the operand's row of this lane's column (the last row past the end)
+        const uint32_t off = (uint32_t)min(gcol, n_grp - 1 - gb) * (uint32_t)(D * 2) + ks_lane;
+        const char *rowp = reinterpret_cast<const char *>(ks + (size_t)(g_first + gb) * D) + off;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int w = (qd >> 1) * KB + kb;
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
-                ksr[kb][hf] = *reinterpret_cast<const uint2 *>(
-                    ks + (size_t)gs * D + 16 * w + 4 * (qd & 1) + 8 * hf);
-        }
+                ksr[kb][hf] = *reinterpret_cast<const uint2 *>(rowp + 2 * (16 * kb + 8 * hf));
     };
     // key zeros, rows = the 16 groups of the window [16 m, 16 m + 16) of
     // wave-relative groups that holds tok's group (a window spans 16 / NG key
@@ -345,12 +347,16 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     };
     typedef uint32_t KWords[KP][TPB][KB];         // key words of a batch
     KWords kw;
-    // tile j's words of the batch at tok
+    // tile j's words of the batch at tok: the tile's first row is uniform
+    // (a tile past the end takes the last tile's rows, never read), the
+    // lane's row and k-block a fixed offset
+    const uint32_t kw_lane = (uint32_t)(r * KW + (qd >> 1) * KB) * 4u;   // bytes
     auto load_ktile = [&](int tok, int j, KWords &kw) {
-        const int t = min(tok + 16 * j + r, nt - 1);
+        const int ts = min(tok + 16 * j, nt - 16);
 #pragma unroll
         for (int pl = 0; pl < KP; ++pl) {
-            const uint32_t *wp = kq + pl * kpl + (uint32_t)((t0 + t) * KW + (qd >> 1) * KB);
+            const uint32_t *wp = reinterpret_cast<const uint32_t *>(
+                reinterpret_cast<const char *>(kq + pl * kpl + (size_t)(t0 + ts) * KW) + kw_lane);
             if constexpr (KB == 4) {
                 const uint4 x = *reinterpret_cast<const uint4 *>(wp);
                 kw[pl][j][0] = x.x; kw[pl][j][1] = x.y; kw[pl][j][2] = x.z; kw[pl][j][3] = x.w;
@@ -663,16 +669,29 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     if constexpr (!ONE && !PF)
 #pragma unroll
         for (int k = 0; k < NK; ++k) load_vmeta(k);
+    // every logit of the lane's tokens is read first (one LDS wait, not one
+    // per token and head); slots past the wave's tokens hold stale values
+    // that only meet a select, and slots past nt32 are never read by phase V
+    float lgv[NK][G];
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int h = 0; h < G; ++h) lgv[k][h] = L.ls[h * kLsStride + lane + 64 * k];
+    // (an empty asm use keeps the reads here rather than sunk into the
+    // token loop below, one wait per 64 tokens)
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int h = 0; h < G; ++h) asm volatile("" : : "v"(lgv[k][h]));
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
         const int t = lane + 64 * k;
         if (64 * k >= nt32) break;                // uniform
-        if (t >= nt32) continue;
         const bool ok = t < nt;
         const float q4 = __builtin_amdgcn_ldexpf(1.f, -2 * (t & 3));
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float p = ok ? __builtin_amdgcn_exp2f(L.ls[h * kLsStride + t] - m_h[h]) : 0.f;
+            const float p = ok ? __builtin_amdgcn_exp2f(lgv[k][h] - m_h[h]) : 0.f;
             l_h[h] += p;
             L.ls[h * kLsStride + t] = p * q4;
         }
