@@ -996,10 +996,13 @@ __device__ __forceinline__ void residual_wave(const DecArgs &a, int unit, int t0
 // FULLV: value channel groups of 16 (D/16 scales per token).
 // MASS: also store every token's logit for the persistence audit.
 // W: waves per block, each with a chunk / W share of the split's tokens.
-// KP, VP: 2-bit planes of the key / value codes (packed_wave).
+// KP, VP: 2-bit planes of the key / value codes (packed_wave).  Blocks per
+// SIMD: 4 for the INT2 g = 1 kernel, 2 where the registers need it (g = 2
+// and 8, 8-bit keys, 4-bit keys and values at g = 4, which at 3 would
+// spill), else 3.
 template <int D, int G, bool FULLV, bool ONE, bool MASS, int W = kWaves, int KP = 1,
           int VP = 1>
-__global__ __launch_bounds__(W * 64, (G == 2 || G == 8 || KP == 4) ? 2 : (G == 1 && !ONE && KP == 1 && VP == 1) ? 4 : 3) void decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(W * 64, (G == 2 || G == 8 || KP == 4 || (G == 4 && KP == 2 && VP == 2)) ? 2 : (G == 1 && !ONE && KP == 1 && VP == 1) ? 4 : 3) void decode_kernel(DecArgs a) {
     // x = unit, y = split: with the round-robin dispatch of workgroups over
     // the 8 XCDs, every split of a unit (and its merge below) runs on the
     // XCD unit mod 8 when the unit count is a multiple of 8.
