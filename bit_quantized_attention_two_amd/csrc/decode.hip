@@ -86,6 +86,12 @@ struct DecArgs {
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// Views of the per-wave LDS rows whose contents change type between phases
+// (fp32 logits, then fp16 probability parts read as dwords): accesses
+// through them may alias any other, so no load or store is moved across
+// one of another type.
+typedef _Float16 half_ma __attribute__((may_alias));
+typedef unsigned int u32x4_ma __attribute__((ext_vector_type(4), may_alias));
 
 // 16x16x32 fp16 MFMA: A lane l holds A[l%16][8(l/16)+j], B lane l holds
 // B[8(l/16)+j][l%16], C lane l register i holds C[4(l/16)+i][l%16].
@@ -216,15 +222,24 @@ __device__ __forceinline__ void unpack8h(uint4 x, float *f) {
     for (int i = 0; i < 8; ++i) f[i] = h2f((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
 }
 
-// Per-wave LDS.  `ls` holds the logits of the wave's tokens, then their
-// probabilities times 4^-(t%4), [h][t]; at the end, aliased, the wave's
-// unnormalised output [h][D].  `sv` / `zv` hold the value scales and
-// zero-points per 16-channel group and token, [g16][t] (a value group of
-// more than 16 channels repeats its scale in each of its 16-channel parts).
-// Row strides are padded so that rows read by different lanes fall in
-// different LDS banks.
+// Per-wave LDS.  `ls` holds the logits of the wave's tokens, [h][t]; then
+// each head's row holds the probabilities times 4^-(t%4) as two fp16 parts,
+// hi at halves [0, 256) and lo at [kPLo, kPLo + 256) of the row, at token
+// slot pslot(t); at the end, aliased, the wave's unnormalised output [h][D].
+// `sv` / `zv` hold the value scales and zero-points per 16-channel group,
+// [g16][pslot(t)] (a value group of more than 16 channels repeats its
+// scale in each of its 16-channel parts).  Row strides are padded so that
+// rows read by different lanes fall in different LDS banks.
 constexpr int kLsStride = kMaxWaveChunk + 4;      // floats
 constexpr int kSvStride = kMaxWaveChunk + 8;      // halves
+constexpr int kPLo = kMaxWaveChunk + 8;           // halves: lo parts (16-byte aligned)
+static_assert(kPLo + kMaxWaveChunk <= 2 * kLsStride, "both parts fit a row");
+// Token t's slot: within each 16-token block, tokens t and t + 8 side by
+// side, so that one dword holds the pair (t, t + 8) that a value B-operand
+// dword takes (its low and high half).
+__device__ __forceinline__ int pslot(int t) {
+    return (t & ~15) | ((t & 7) << 1) | ((t >> 3) & 1);
+}
 template <int D, int G>
 struct alignas(16) WaveLds {
     static constexpr int NG16 = D / 16;
@@ -683,25 +698,34 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     for (int k = 0; k < NK; ++k)
 #pragma unroll
         for (int h = 0; h < G; ++h) asm volatile("" : : "v"(lgv[k][h]));
+    // (every logit is in registers now, so the rows can take the fp16
+    // parts, at other slots, without overwriting an unread logit)
+    half_ma *const ph = reinterpret_cast<half_ma *>(L.ls);
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
         const int t = lane + 64 * k;
         if (64 * k >= nt32) break;                // uniform
         const bool ok = t < nt;
+        const int ps = pslot(t);
         const float q4 = __builtin_amdgcn_ldexpf(1.f, -2 * (t & 3));
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float p = ok ? __builtin_amdgcn_exp2f(lgv[k][h] - m_h[h]) : 0.f;
             l_h[h] += p;
-            L.ls[h * kLsStride + t] = p * q4;
+            // p 4^-i as hi + lo: hi rounded to fp16, lo = the exact fp32
+            // remainder rounded to fp16
+            const float w = p * q4;
+            const half_t whi = (half_t)w;
+            ph[h * 2 * kLsStride + ps] = whi;
+            ph[h * 2 * kLsStride + kPLo + ps] = (half_t)(w - (float)whi);
         }
 #pragma unroll
         for (int j = 0; j < MW; ++j) {
             const uint32_t sw = ok ? msr[k][j] : 0u, zw = ok ? mzr[k][j] : 0u;
-            L.sv[(2 * j) * kSvStride + t] = __builtin_bit_cast(half_t, (uint16_t)(sw & 0xffffu));
-            L.sv[(2 * j + 1) * kSvStride + t] = __builtin_bit_cast(half_t, (uint16_t)(sw >> 16));
-            L.zv[(2 * j) * kSvStride + t] = __builtin_bit_cast(half_t, (uint16_t)(zw & 0xffffu));
-            L.zv[(2 * j + 1) * kSvStride + t] = __builtin_bit_cast(half_t, (uint16_t)(zw >> 16));
+            L.sv[(2 * j) * kSvStride + ps] = __builtin_bit_cast(half_t, (uint16_t)(sw & 0xffffu));
+            L.sv[(2 * j + 1) * kSvStride + ps] = __builtin_bit_cast(half_t, (uint16_t)(sw >> 16));
+            L.zv[(2 * j) * kSvStride + ps] = __builtin_bit_cast(half_t, (uint16_t)(zw & 0xffffu));
+            L.zv[(2 * j + 1) * kSvStride + ps] = __builtin_bit_cast(half_t, (uint16_t)(zw >> 16));
         }
     }
 #pragma unroll
@@ -732,29 +756,30 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     // the last step's LDS rows and multiplies with zero probabilities, so
     // it adds exactly nothing; the step pair then has no branch, and the
     // loads two steps ahead keep their place in the wait counts.
+    // the lane's 8 token slots of a step: tokens tb + i and tb + 8 + i side
+    // by side (pslot), as dword i of its B operand takes them
+    const int pb0 = 16 * (qd >> 1) + 8 * (qd & 1);
+    const half_ma *const phr = reinterpret_cast<const half_ma *>(L.ls) + hc * 2 * kLsStride;
     auto step = [&](int e, bool live, auto &&code, auto &&after) {
-        const int st = 32 * min(e, nsteps - 1);
-        const float *pp = &L.ls[hc * kLsStride + st + tb];
-        float4_t p0 = *reinterpret_cast<const float4_t *>(pp);
-        float4_t p1 = *reinterpret_cast<const float4_t *>(pp + 8);
+        const int pb = 32 * min(e, nsteps - 1) + pb0;
+        const half8_t phv = *reinterpret_cast<const half8_t *>(phr + pb);
+        const half8_t plv = *reinterpret_cast<const half8_t *>(phr + kPLo + pb);
+        u32x4 phi = __builtin_bit_cast(u32x4, phv);
+        u32x4 plo = __builtin_bit_cast(u32x4, plv);
         // several passes: every pass's scale and zero reads up front, so the
         // step waits for LDS once
-        half4_t s0h[NPASS], s1h[NPASS], z0h[NPASS], z1h[NPASS];
+        u32x4 svh[NPASS], zvh[NPASS];
         auto read_meta = [&](int P) {
             const int vg = P * GPP + r % GPP;
-            const half_t *sp = &L.sv[vg * kSvStride + st + tb];
-            const half_t *zp = &L.zv[vg * kSvStride + st + tb];
-            s0h[P] = *reinterpret_cast<const half4_t *>(sp);
-            s1h[P] = *reinterpret_cast<const half4_t *>(sp + 8);
-            z0h[P] = *reinterpret_cast<const half4_t *>(zp);
-            z1h[P] = *reinterpret_cast<const half4_t *>(zp + 8);
+            svh[P] = *reinterpret_cast<const u32x4_ma *>(&L.sv[vg * kSvStride + pb]);
+            zvh[P] = *reinterpret_cast<const u32x4_ma *>(&L.zv[vg * kSvStride + pb]);
         };
         if constexpr (NPASS > 1)
 #pragma unroll
             for (int P = 0; P < NPASS; ++P) read_meta(P);
         if (!live) {
-            p0 = float4_t{0.f, 0.f, 0.f, 0.f};
-            p1 = float4_t{0.f, 0.f, 0.f, 0.f};
+            phi = u32x4{0u, 0u, 0u, 0u};
+            plo = u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int P = 0; P < NPASS; ++P) {
@@ -769,18 +794,26 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             }
             after(P);
             if constexpr (NPASS == 1) read_meta(P);
-            const half4_t s0 = s0h[P], s1 = s1h[P], z0 = z0h[P], z1 = z1h[P];
             u32x4 bhw, blw;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                uint32_t hw, lw;
-                split2x2(__builtin_fmaf(p0[i], (float)s0[i], 0.f),
-                         __builtin_fmaf(p1[i], (float)s1[i], 0.f), hw, lw);
-                bhw[i] = hw;
-                blw[i] = lw;
+                // weights (p 4^-i) s as hi + lo: the TwoProduct of the hi
+                // part and s, plus the lo part times s
+                // (each vector element copied out first: a bit cast of an
+                // element of a vector-typed value reads element 0)
+                const uint32_t ahw = phi[i], alw = plo[i], scw = svh[P][i], zcw = zvh[P][i];
+                const half2_t ah = __builtin_bit_cast(half2_t, ahw);
+                const half2_t al = __builtin_bit_cast(half2_t, alw);
+                const half2_t sc = __builtin_bit_cast(half2_t, scw);
+                const half2_t zc = __builtin_bit_cast(half2_t, zcw);
+                const half2_t wh = ah * sc;
+                const half2_t wl = __builtin_elementwise_fma(
+                    al, sc, __builtin_elementwise_fma(ah, sc, -wh));
+                bhw[i] = __builtin_bit_cast(uint32_t, wh);
+                blw[i] = __builtin_bit_cast(uint32_t, wl);
                 // p is stored times 4^-i: keep one z sum per i
-                za[P][i] = __builtin_fmaf(p0[i], (float)z0[i], za[P][i]);
-                za[P][i] = __builtin_fmaf(p1[i], (float)z1[i], za[P][i]);
+                za[P][i] = __builtin_amdgcn_fdot2(ah, zc, za[P][i], false);
+                za[P][i] = __builtin_amdgcn_fdot2(al, zc, za[P][i], false);
             }
             const half8_t bh = __builtin_bit_cast(half8_t, bhw);
             const half8_t bl = __builtin_bit_cast(half8_t, blw);
