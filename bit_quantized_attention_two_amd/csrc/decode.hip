@@ -832,11 +832,17 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         }
     } else {
         // value words two steps ahead: buffer A holds even steps, B odd
+        // (issued A before B, as the loop issues them, so that the waits
+        // at the loop's top, which merge this order with the loop's own,
+        // leave B's words in flight while A's are used)
         if constexpr (!PF) {
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int P = 0; P < NPASS; ++P) load_vw(P, 0, vwA[P]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int P = 0; P < NPASS; ++P) load_vw(P, min(32, nt32 - 32), vwB[P]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         auto pair = [&](int e, bool full) {
             step(e, true, [&](int P, int mb) { return vwA[P][mb]; }, [&](int P) {
