@@ -269,7 +269,7 @@ struct alignas(16) WaveLds {
 // KP, VP: 2-bit planes of the key and value codes (1: INT2; 2: 4-bit codes,
 // combined into one code operand; KP 4: 8-bit keys as a low and a high
 // 4-bit operand with their own accumulators, logit = low + 16 high).
-template <int D, int G, bool FULLV, bool ONE, bool MASS, int KP = 1, int VP = 1>
+template <int D, int G, bool FULLV, bool ONE, bool MASS, int KP = 1, int VP = 1, bool SL = false>
 __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                                             int nt, WaveLds<D, G> &L,
                                             float *m_out, float *l_out) {
@@ -579,7 +579,18 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     // kernels have the registers to spare at their occupancy).
     constexpr bool PF = G > 1 && !ONE && KP < 4;
     const int nt32 = (nt + 31) & ~31;
-    uint32_t vwA[NPASS][MBP * VP], vwB[NPASS][MBP * VP];   // value words, even / odd steps
+    // Value words: the loop keeps two steps in flight (A even steps, B
+    // odd); the straight-line steps of a full wave share (SL: several
+    // passes, nt32 = kMaxWaveChunk) keep three, in A, B and C by step mod 3.
+    // The two forms are separate instances, so that neither moves the
+    // other's in-flight value registers (a copy of a register a load has
+    // not yet filled waits for every load).
+    // (16-channel value groups and keys of at most 4 bits: with wider
+    // groups the extra buffer spills, and 8-bit keys measured slower;
+    // those keep the pair steps below in one instance)
+    constexpr bool SLF = FULLV && !ONE && KP < 4 && NPASS > 1;
+    static_assert(!SL || SLF, "straight-line form: several passes");
+    uint32_t vwA[NPASS][MBP * VP], vwB[NPASS][MBP * VP], vwC[NPASS][MBP * VP];
     auto load_v_first = [&]() {
 #pragma unroll
         for (int k = 0; k < NK; ++k) load_vmeta(k);
@@ -587,6 +598,9 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         for (int P = 0; P < NPASS; ++P) load_vw(P, 0, vwA[P]);
 #pragma unroll
         for (int P = 0; P < NPASS; ++P) load_vw(P, min(32, nt32 - 32), vwB[P]);
+        if constexpr (SL)
+#pragma unroll
+            for (int P = 0; P < NPASS; ++P) load_vw(P, 64, vwC[P]);
     };
     // One key batch.  The next batch's words of tile j are requested into
     // tile j's registers as soon as its MFMAs have read them, so each tile's
@@ -843,6 +857,10 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
 #pragma unroll
             for (int P = 0; P < NPASS; ++P) load_vw(P, min(32, nt32 - 32), vwB[P]);
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (SL)
+#pragma unroll
+                for (int P = 0; P < NPASS; ++P) load_vw(P, 64, vwC[P]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         auto pair = [&](int e, bool full) {
             step(e, true, [&](int P, int mb) { return vwA[P][mb]; }, [&](int P) {
@@ -856,11 +874,34 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
-        if (NPASS > 1 && nsteps == kMaxWaveChunk / 32) {
+        // step e of the straight-line form: its words in buffer e mod 3,
+        // which then takes step e + 3's
+        auto tri = [&](auto ec) {
+            constexpr int e = decltype(ec)::value;
+            uint32_t(&buf)[NPASS][MBP * VP] = e % 3 == 0 ? vwA : e % 3 == 1 ? vwB : vwC;
+            step(e, true, [&](int P, int mb) { return buf[P][mb]; }, [&](int P) {
+                if constexpr (e + 3 < kMaxWaveChunk / 32) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_vw(P, 32 * (e + 3), buf[P]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            });
+        };
+        if constexpr (SL) {
             // a full wave share: straight-line steps, so each wait for the
-            // value words leaves the next step's loads in flight (in the
-            // loop the compiler waits for all of them); one pass (g = 1)
+            // value words leaves the next two steps' loads in flight (in
+            // the loop the compiler waits for all of them); one pass (g = 1)
             // keeps the loop, whose registers then fit four waves per SIMD
+            tri(std::integral_constant<int, 0>{});
+            tri(std::integral_constant<int, 1>{});
+            tri(std::integral_constant<int, 2>{});
+            tri(std::integral_constant<int, 3>{});
+            tri(std::integral_constant<int, 4>{});
+            tri(std::integral_constant<int, 5>{});
+            tri(std::integral_constant<int, 6>{});
+            tri(std::integral_constant<int, 7>{});
+        } else if (!SLF && NPASS > 1 && nsteps == kMaxWaveChunk / 32) {
+            // the same two steps ahead (A / B), straight-line
 #pragma unroll
             for (int e = 0; e < kMaxWaveChunk / 32; e += 2) pair(e, true);
         } else {
@@ -1072,8 +1113,17 @@ __global__ __launch_bounds__(W * 64, (G == 2 || G == 8 || KP == 4 || (G == 4 && 
         const int wchunk = a.chunk / W;
         const int t0 = split * a.chunk + wave * wchunk;
         const int nt = max(0, min(wchunk, n_packed - t0));
-        if (nt > 0)
+        // a full share (the last 32-token step may be partial) takes the
+        // straight-line value steps where there are several value passes
+        constexpr bool SLF = FULLV && !ONE && KP < 4 && (G * (D / 16) + 15) / 16 > 1;
+        if constexpr (SLF) {
+            if (nt > kMaxWaveChunk - 32)
+                packed_wave<D, G, FULLV, ONE, MASS, KP, VP, true>(a, unit, t0, nt, lds[wave], m_w, l_w);
+            else if (nt > 0)
+                packed_wave<D, G, FULLV, ONE, MASS, KP, VP>(a, unit, t0, nt, lds[wave], m_w, l_w);
+        } else if (nt > 0) {
             packed_wave<D, G, FULLV, ONE, MASS, KP, VP>(a, unit, t0, nt, lds[wave], m_w, l_w);
+        }
     } else if (res_role) {
         const int nrw = W - a.res_wave0, rw = wave - a.res_wave0;
         const int per = (a.n_res + nrw - 1) / nrw;
