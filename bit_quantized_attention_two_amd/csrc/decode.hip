@@ -581,7 +581,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     const int nt32 = (nt + 31) & ~31;
     // Value words: the loop keeps two steps in flight (A even steps, B
     // odd); the straight-line steps of a full wave share (SL: several
-    // passes, nt32 = kMaxWaveChunk) keep three, in A, B and C by step mod 3.
+    // passes, nt32 = kMaxWaveChunk) keep NVB, in buffer step mod NVB.
     // The two forms are separate instances, so that neither moves the
     // other's in-flight value registers (a copy of a register a load has
     // not yet filled waits for every load).
@@ -590,7 +590,11 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     // those keep the pair steps below in one instance)
     constexpr bool SLF = FULLV && !ONE && KP < 4 && NPASS > 1;
     static_assert(!SL || SLF, "straight-line form: several passes");
-    uint32_t vwA[NPASS][MBP * VP], vwB[NPASS][MBP * VP], vwC[NPASS][MBP * VP];
+    // value-word buffers (4-bit values: three measured faster than four)
+    constexpr int NVB = !SL ? 2 : VP == 1 ? 4 : 3;
+    uint32_t vwS[NVB][NPASS][MBP * VP];
+    uint32_t(&vwA)[NPASS][MBP * VP] = vwS[0];
+    uint32_t(&vwB)[NPASS][MBP * VP] = vwS[1];
     auto load_v_first = [&]() {
 #pragma unroll
         for (int k = 0; k < NK; ++k) load_vmeta(k);
@@ -600,7 +604,9 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         for (int P = 0; P < NPASS; ++P) load_vw(P, min(32, nt32 - 32), vwB[P]);
         if constexpr (SL)
 #pragma unroll
-            for (int P = 0; P < NPASS; ++P) load_vw(P, 64, vwC[P]);
+            for (int e = 2; e < NVB; ++e)
+#pragma unroll
+                for (int P = 0; P < NPASS; ++P) load_vw(P, 32 * e, vwS[e][P]);
     };
     // One key batch.  The next batch's words of tile j are requested into
     // tile j's registers as soon as its MFMAs have read them, so each tile's
@@ -859,8 +865,11 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (SL)
 #pragma unroll
-                for (int P = 0; P < NPASS; ++P) load_vw(P, 64, vwC[P]);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int e = 2; e < NVB; ++e) {
+#pragma unroll
+                    for (int P = 0; P < NPASS; ++P) load_vw(P, 32 * e, vwS[e][P]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
         }
         auto pair = [&](int e, bool full) {
             step(e, true, [&](int P, int mb) { return vwA[P][mb]; }, [&](int P) {
@@ -874,22 +883,22 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
-        // step e of the straight-line form: its words in buffer e mod 3,
-        // which then takes step e + 3's
+        // step e of the straight-line form: its words in buffer e mod NVB,
+        // which then takes step e + NVB's
         auto tri = [&](auto ec) {
             constexpr int e = decltype(ec)::value;
-            uint32_t(&buf)[NPASS][MBP * VP] = e % 3 == 0 ? vwA : e % 3 == 1 ? vwB : vwC;
+            uint32_t(&buf)[NPASS][MBP * VP] = vwS[e % NVB];
             step(e, true, [&](int P, int mb) { return buf[P][mb]; }, [&](int P) {
-                if constexpr (e + 3 < kMaxWaveChunk / 32) {
+                if constexpr (e + NVB < kMaxWaveChunk / 32) {
                     __builtin_amdgcn_sched_barrier(0);
-                    load_vw(P, 32 * (e + 3), buf[P]);
+                    load_vw(P, 32 * (e + NVB), buf[P]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             });
         };
         if constexpr (SL) {
             // a full wave share: straight-line steps, so each wait for the
-            // value words leaves the next two steps' loads in flight (in
+            // value words leaves the next steps' loads in flight (in
             // the loop the compiler waits for all of them); one pass (g = 1)
             // keeps the loop, whose registers then fit four waves per SIMD
             tri(std::integral_constant<int, 0>{});
