@@ -305,7 +305,11 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     const uint16_t *vz = c.vz + (size_t)unit * c.vm_unit();
     const int g_first = t0 >> gk_sh;
     const int n_grp = nt >> gk_sh;
-    const int nbatch = (nt + BT - 1) / BT;
+    // (a full share, SL, has every batch: nt > kMaxWaveChunk - 32); the
+    // 2-bit form takes them as straight-line code (the 4-bit forms measured
+    // slower so)
+    constexpr bool SLK = SL && KP == 1 && VP == 1;
+    const int nbatch = SLK ? kMaxWaveChunk / BT : (nt + BT - 1) / BT;
     const int bb_sh = NG_SH + gk_sh;
     const int bblk = 1 << bb_sh;                  // tokens per key B operand (NG Gk)
     const int last = (nbatch - 1) * BT;           // start of the last batch
@@ -684,7 +688,13 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         }
     };
     if constexpr (PF) {
-        for (int b = 0; b + 1 < nbatch; ++b) kbatch(b, std::false_type{});
+        if constexpr (SLK) {
+            // straight-line batches
+#pragma unroll
+            for (int b = 0; b + 1 < kMaxWaveChunk / BT; ++b) kbatch(b, std::false_type{});
+        } else {
+            for (int b = 0; b + 1 < nbatch; ++b) kbatch(b, std::false_type{});
+        }
         kbatch(nbatch - 1, std::true_type{});
     } else {
         for (int b = 0; b < nbatch; ++b) kbatch(b, std::false_type{});
