@@ -591,11 +591,14 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     // not yet filled waits for every load).
     // (16-channel value groups and keys of at most 4 bits: with wider
     // groups the extra buffer spills, and 8-bit keys measured slower;
-    // those keep the pair steps below in one instance)
-    constexpr bool SLF = FULLV && !ONE && KP < 4 && NPASS > 1;
-    static_assert(!SL || SLF, "straight-line form: several passes");
+    // those keep the pair steps below in one instance; g = 1, one pass,
+    // 2-bit codes: two buffers, four waves per SIMD without the mass
+    // audit's stores; its 4-bit forms measured slower so)
+    constexpr bool SLF = FULLV && !ONE && KP < 4 &&
+                         (NPASS > 1 || (G == 1 && !MASS && KP == 1 && VP == 1));
+    static_assert(!SL || SLF, "straight-line form: see SLF");
     // value-word buffers (4-bit values: three measured faster than four)
-    constexpr int NVB = !SL ? 2 : VP == 1 ? 4 : 3;
+    constexpr int NVB = !SL || G == 1 ? 2 : VP == 1 ? 4 : 3;
     uint32_t vwS[NVB][NPASS][MBP * VP];
     uint32_t(&vwA)[NPASS][MBP * VP] = vwS[0];
     uint32_t(&vwB)[NPASS][MBP * VP] = vwS[1];
@@ -908,9 +911,7 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
         };
         if constexpr (SL) {
             // a full wave share: straight-line steps, so each wait for the
-            // value words leaves the next steps' loads in flight (in
-            // the loop the compiler waits for all of them); one pass (g = 1)
-            // keeps the loop, whose registers then fit four waves per SIMD
+            // value words leaves the next steps' loads in flight
             tri(std::integral_constant<int, 0>{});
             tri(std::integral_constant<int, 1>{});
             tri(std::integral_constant<int, 2>{});
@@ -1133,8 +1134,10 @@ __global__ __launch_bounds__(W * 64, (G == 2 || G == 8 || KP == 4 || (G == 4 && 
         const int t0 = split * a.chunk + wave * wchunk;
         const int nt = max(0, min(wchunk, n_packed - t0));
         // a full share (the last 32-token step may be partial) takes the
-        // straight-line value steps where there are several value passes
-        constexpr bool SLF = FULLV && !ONE && KP < 4 && (G * (D / 16) + 15) / 16 > 1;
+        // straight-line instance where it exists (SLF in packed_wave)
+        constexpr bool SLF = FULLV && !ONE && KP < 4 &&
+                             ((G * (D / 16) + 15) / 16 > 1 ||
+                              (G == 1 && !MASS && KP == 1 && VP == 1));
         if constexpr (SLF) {
             if (nt > kMaxWaveChunk - 32)
                 packed_wave<D, G, FULLV, ONE, MASS, KP, VP, true>(a, unit, t0, nt, lds[wave], m_w, l_w);
