@@ -590,15 +590,16 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     // other's in-flight value registers (a copy of a register a load has
     // not yet filled waits for every load).
     // (16-channel value groups and keys of at most 4 bits: with wider
-    // groups the extra buffer spills, and 8-bit keys measured slower;
-    // those keep the pair steps below in one instance; g = 1, one pass,
-    // 2-bit codes: two buffers, four waves per SIMD without the mass
+    // value groups this instance spilled, and 8-bit keys measured slower;
+    // those keep the pair steps below in one instance.  g = 1, one pass:
+    // 2-bit codes only, which fit four waves per SIMD without the mass
     // audit's stores; its 4-bit forms measured slower so)
     constexpr bool SLF = FULLV && !ONE && KP < 4 &&
                          (NPASS > 1 || (G == 1 && !MASS && KP == 1 && VP == 1));
     static_assert(!SL || SLF, "straight-line form: see SLF");
-    // value-word buffers (4-bit values: three measured faster than four)
-    constexpr int NVB = !SL || G == 1 ? 2 : VP == 1 ? 4 : 3;
+    // value-word buffers: 4-bit values three; 2-bit values two (three or
+    // four measured slower)
+    constexpr int NVB = SL && VP == 2 ? 3 : 2;
     uint32_t vwS[NVB][NPASS][MBP * VP];
     uint32_t(&vwA)[NPASS][MBP * VP] = vwS[0];
     uint32_t(&vwB)[NPASS][MBP * VP] = vwS[1];
