@@ -269,6 +269,8 @@ struct alignas(16) WaveLds {
 // KP, VP: 2-bit planes of the key and value codes (1: INT2; 2: 4-bit codes,
 // combined into one code operand; KP 4: 8-bit keys as a low and a high
 // 4-bit operand with their own accumulators, logit = low + 16 high).
+// SL: the instance for a full wave share (straight-line steps; SLF below
+// names the forms that have it).
 template <int D, int G, bool FULLV, bool ONE, bool MASS, int KP = 1, int VP = 1, bool SL = false>
 __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
                                             int nt, WaveLds<D, G> &L,
@@ -583,22 +585,23 @@ __device__ __forceinline__ void packed_wave(const DecArgs &a, int unit, int t0,
     // kernels have the registers to spare at their occupancy).
     constexpr bool PF = G > 1 && !ONE && KP < 4;
     const int nt32 = (nt + 31) & ~31;
-    // Value words: the loop keeps two steps in flight (A even steps, B
-    // odd); the straight-line steps of a full wave share (SL: several
-    // passes, nt32 = kMaxWaveChunk) keep NVB, in buffer step mod NVB.
-    // The two forms are separate instances, so that neither moves the
-    // other's in-flight value registers (a copy of a register a load has
-    // not yet filled waits for every load).
-    // (16-channel value groups and keys of at most 4 bits: with wider
-    // value groups this instance spilled, and 8-bit keys measured slower;
-    // those keep the pair steps below in one instance.  g = 1, one pass:
-    // 2-bit codes only, which fit four waves per SIMD without the mass
-    // audit's stores; its 4-bit forms measured slower so)
+    // Value words: NVB steps in flight, in buffer step mod NVB (A even
+    // steps, B odd when NVB = 2).  A full wave share (nt32 = kMaxWaveChunk)
+    // of the forms SLF names runs as its own instance (SL), whose value
+    // steps, and for 2-bit codes key batches, are straight-line code: in
+    // one instance with the loop form, the register allocator moved the
+    // value buffers where the two paths part, and a copy of a register whose
+    // load is still in flight waits for every load.
+    // SLF: 16-channel value groups and keys of at most 4 bits with several
+    // value passes (wider value groups spilled in this instance, 8-bit keys
+    // measured slower; those keep the pair steps below in one instance), or
+    // g = 1 with 2-bit codes (four waves per SIMD without the mass audit's
+    // stores; its 4-bit forms measured slower).
     constexpr bool SLF = FULLV && !ONE && KP < 4 &&
                          (NPASS > 1 || (G == 1 && !MASS && KP == 1 && VP == 1));
     static_assert(!SL || SLF, "straight-line form: see SLF");
-    // value-word buffers: 4-bit values three; 2-bit values two (three or
-    // four measured slower)
+    // 4-bit values three buffers; 2-bit values two (three or four measured
+    // slower)
     constexpr int NVB = SL && VP == 2 ? 3 : 2;
     uint32_t vwS[NVB][NPASS][MBP * VP];
     uint32_t(&vwA)[NPASS][MBP * VP] = vwS[0];
