@@ -119,6 +119,30 @@ def test_mikv_pack_decode(bits_hi, bits_lo, D, Gk, n, n_sel):
         _decode_compare(torch, mk, dims, gc, oc, q, units, "after pack")
 
 
+@pytest.mark.parametrize("g,bits_hi,bits_lo", [(4, (4, 4), (2, 2)), (4, (4, 2), (2, 2)),
+                                               (4, (8, 4), (4, 2)), (8, (4, 4), (2, 2))])
+def test_mixed_full_wave_shares(g, bits_hi, bits_lo):
+    """A first segment of 2288 tokens per unit over 128 units, so that its
+    split plan takes 256-token wave shares: eight full ones and one of 240
+    per unit, the shares that run as straight-line code in the 4-bit forms
+    (INT4 keys and values at g = 4 and 8, 4-bit keys with 2-bit values),
+    and the 8-bit-key form next to them; 12 sampled units packed bit for
+    bit and decoded against the oracle."""
+    torch, mk = require_gpu()
+    B, Hkv, D, Gk = 4, 32, 128, 16
+    n_sel = 8 * 256 + 240
+    n = n_sel + 512
+    say("mixed-full-shares", dict(g=g, bits=(bits_hi, bits_lo), n=n, n_sel=n_sel))
+    dims, gc, oc = _mikv_build(torch, mk, B, Hkv, g, D, Gk, n, n_sel, bits_hi, bits_lo,
+                               seed=500 + g + bits_hi[0] + bits_hi[1])
+    units = [(b, h) for b in range(B) for h in range(Hkv)]
+    rr = np.random.default_rng(g + 10 * bits_hi[0] + bits_hi[1])
+    units = [units[i] for i in sorted(rr.choice(len(units), 12, replace=False))]
+    _compare_mixed(torch, gc, oc, units, "after pack")
+    q, _, _ = synth.gen_decode_step(11, 0, n, B, Hkv * g, Hkv, D)
+    _decode_compare(torch, mk, dims, gc, oc, q, units, "after pack")
+
+
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
 def test_mikv_appends_and_flush(g):
     torch, mk = require_gpu()
