@@ -284,7 +284,8 @@ def test_append_decode_equals_separate_calls(g, D, B, Hkv, n, m):
     (1, 2, 4, 64, 32, 16, 900, 500),
     (2, 2, 2, 128, 16, 32, 700, 330),
     (8, 32, 1, 128, 16, 16, 2200, 2100),  # multi-batch waves
-])
+    (9, 32, 4, 128, 16, 16, 2400, 2293),  # 256- and 240-token shares, 4-wave
+])                                        # blocks for both calls (288 units)
 def test_decode_mass_matches_oracle(B, Hkv, g, D, Gk, Gv, n, m):
     """Persistence audit: minikv_decode_attn_mass gives decode_attn's o bit
     for bit, and accumulates every cached token's attention weight (summed
