@@ -204,23 +204,23 @@ def test_decode_multi_batch_waves(D, g, Gv):
     _decode_and_compare(torch, mk, dims, cache, oc, q, units)
 
 
-@pytest.mark.parametrize("g", [1, 4, 8])
-def test_decode_full_and_partial_wave_shares(g):
+@pytest.mark.parametrize("g,D", [(1, 128), (4, 128), (8, 128), (1, 64), (8, 64)])
+def test_decode_full_and_partial_wave_shares(g, D):
     """Wave shares of 256 tokens (eight full ones per unit) and one of 240
     (its last 32-token value step half past the end): the shares that run
     as straight-line code, full and partial, next to a short one; 256 units
     so that the split plan picks 256-token shares (the 12-wave form at
-    g = 4, the 4-wave form at g = 1 and 8).  16 sampled units against the
-    oracle."""
+    g = 4, the 4-wave form at g = 1 and 8; at D = 64 too).  16 sampled
+    units against the oracle."""
     torch, mk = require_gpu()
-    B, Hkv, D, n = 8, 32, 128, 2400
+    B, Hkv, n = 8, 32, 2400
     m = 8 * 256 + 240 + 5                         # 2288 packed + 5 residual
-    say("decode-full-partial-shares", dict(g=g, n=n, m=m))
+    say("decode-full-partial-shares", dict(g=g, D=D, n=n, m=m))
     units = [(b, h) for b in range(B) for h in range(Hkv)]
-    rr = np.random.default_rng(70 + g)
+    rr = np.random.default_rng(70 + g + D)
     units = [units[i] for i in sorted(rr.choice(len(units), 16, replace=False))]
     dims, cache, oc = _build(torch, mk, B, Hkv, g, D, 16, 16, n, m,
-                             seed=60 + g, check_bits=False, units=units)
+                             seed=60 + g + D, check_bits=False, units=units)
     q, kn, vn = synth.gen_decode_step(8, 0, 0, B, Hkv * g, Hkv, D)
     mk.append(dims, cache, dev16(torch, kn), dev16(torch, vn))
     oc.append(kn, vn)
